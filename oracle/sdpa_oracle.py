@@ -1,0 +1,311 @@
+"""CPU oracle for scaled dot-product attention: plain, slow, float64.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call this
+module: only the tests, the smoke check in __graft_entry__ and the benchmark's
+CPU-baseline leg use it.  It shares no code with the HIP library and imports
+nothing from it.
+
+What it computes is the plain definition of attention, written out with the
+n x n score matrix S and probability matrix P materialised, in the order the
+pages give it:
+
+  * "Flash Attention原理：分块计算与重计算" (cnblogs), section 一: inputs
+    shaped (batch, num_heads, seq_len, head_dim); S = Q K^T; P = softmax(S /
+    sqrt(d)) taken along the key axis; O = P V.  Its listing applies the scale
+    Q.size(-1) ** -0.5 to S when no scale is given.
+  * "PyTorch Profiler 實戰：五種 Attention 實現的 GPU 核心剖析", section
+    "核心概念": the step order is Q K^T, scale, causal mask, softmax, times V.
+  * The same cnblogs page, section 四: the softmax subtracts the row maximum
+    before exponentiating, and section 五: the per-row statistics kept instead
+    of S and P are the row maximum m and the normaliser l.  Here they are
+    returned together as the natural-log log-sum-exp, LSE = m + ln l.
+
+Readings where the pages leave a step open (each also listed in the design
+notes):
+  * causal means top-left alignment with Lq == Lk: query i sees keys j <= i;
+  * a grouped-query head h reads key/value head h // (Hq / Hkv);
+  * decode is one query token per sequence that sees cache slots 0..L_b-1;
+    a length above the cache size is clamped to it;
+  * a row that sees no key at all gets O = 0 and LSE = -inf.
+
+All functions take and return numpy float64 arrays.
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Iterable, Optional, Sequence
+
+import numpy as np
+
+try:  # keep BLAS single-threaded inside the per-head thread pool
+    from threadpoolctl import threadpool_limits
+except Exception:  # pragma: no cover
+    threadpool_limits = None
+
+
+def default_scale(d: int) -> float:
+    """1/sqrt(d), the default scale of the cnblogs page's section 一 listing."""
+    return 1.0 / math.sqrt(d)
+
+
+def _head_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                    causal: bool, row_ids: Optional[np.ndarray] = None,
+                    n_keys: Optional[int] = None, return_sp: bool = False):
+    """One (batch, head) pair: q [n_rows, d], k and v [Lk, d].
+
+    row_ids are the absolute query positions of the rows of q (needed for the
+    causal mask when only some rows are asked for).  n_keys limits the keys to
+    the first n_keys rows of k and v (decode lengths).
+    """
+    if n_keys is not None:
+        k = k[:n_keys]
+        v = v[:n_keys]
+    n_rows, lk = q.shape[0], k.shape[0]
+    d_v = v.shape[1]
+    if lk == 0:
+        o = np.zeros((n_rows, d_v))
+        lse = np.full(n_rows, -np.inf)
+        if return_sp:
+            return o, lse, np.zeros((n_rows, 0)), np.zeros((n_rows, 0))
+        return o, lse
+    # Step 1: scores, materialised, then scaled.
+    s = (q @ k.T) * scale
+    # Step 2: causal mask.
+    if causal:
+        if row_ids is None:
+            row_ids = np.arange(n_rows)
+        cols = np.arange(lk)
+        s = np.where(cols[None, :] > row_ids[:, None], -np.inf, s)
+    # Step 3: safe softmax along the key axis.
+    m = s.max(axis=-1)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    e = np.exp(s - m_safe[:, None])
+    l = e.sum(axis=-1)
+    l_safe = np.where(empty, 1.0, l)
+    p = e / l_safe[:, None]
+    # Step 4: weighted sum of values.
+    o = p @ v
+    # Step 5: row statistics as one log-sum-exp.
+    with np.errstate(divide="ignore"):
+        lse = np.where(empty, -np.inf, m_safe + np.log(l_safe))
+    o = np.where(empty[:, None], 0.0, o)
+    if return_sp:
+        return o, lse, s, p
+    return o, lse
+
+
+def _as64(x) -> np.ndarray:
+    """Widen to float64 (accepts numpy arrays and CPU torch tensors, bf16 included)."""
+    if hasattr(x, "detach"):
+        import torch
+        x = x.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _pool_map(fn, items: Sequence, threads: Optional[int]):
+    if threads is None:
+        threads = min(len(items), os.cpu_count() or 1)
+    if threads <= 1 or len(items) <= 1:
+        return [fn(it) for it in items]
+    ctx = threadpool_limits(limits=1) if threadpool_limits is not None else None
+    try:
+        if ctx is not None:
+            ctx.__enter__()
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            return list(ex.map(fn, items))
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+
+
+def attention_forward(q, k, v, causal: bool = False, scale: Optional[float] = None,
+                      threads: Optional[int] = None, return_sp: bool = False):
+    """Prefill attention. q [B,Hq,Lq,d]; k, v [B,Hkv,Lk,d] -> O [B,Hq,Lq,d], LSE [B,Hq,Lq].
+
+    With return_sp the materialised S and P [B,Hq,Lq,Lk] are returned as well
+    (small shapes only).
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, Hq, Lq, d = q.shape
+    Bk, Hkv, Lk, dk = k.shape
+    if Bk != B or dk != d or v.shape[:3] != k.shape[:3]:
+        raise ValueError("q, k, v shapes disagree")
+    if Hkv == 0 or Hq % Hkv != 0:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    if causal and Lq != Lk:
+        raise ValueError("causal attention is defined here for Lq == Lk only")
+    if scale is None:
+        scale = default_scale(d)
+    group = Hq // Hkv
+    o = np.zeros((B, Hq, Lq, v.shape[3]))
+    lse = np.zeros((B, Hq, Lq))
+    s_all = np.zeros((B, Hq, Lq, Lk)) if return_sp else None
+    p_all = np.zeros((B, Hq, Lq, Lk)) if return_sp else None
+    items = [(b, h) for b in range(B) for h in range(Hq)]
+
+    def one(item):
+        b, h = item
+        hk = h // group
+        return _head_attention(q[b, h], k[b, hk], v[b, hk], scale, causal,
+                               return_sp=return_sp)
+
+    results = _pool_map(one, items, threads)
+    for (b, h), res in zip(items, results):
+        o[b, h], lse[b, h] = res[0], res[1]
+        if return_sp:
+            s_all[b, h], p_all[b, h] = res[2], res[3]
+    if return_sp:
+        return o, lse, s_all, p_all
+    return o, lse
+
+
+def attention_forward_rows(q, k, v, b: int, h: int, rows: Iterable[int],
+                           causal: bool = False, scale: Optional[float] = None):
+    """The same definition for a few query rows of one (batch, query head).
+
+    Used to check full-size runs on sampled outputs: each row needs only its
+    own score row, so any row of any size can be computed on its own.
+    Returns O [len(rows), d] and LSE [len(rows)].
+    """
+    q_bh = _as64(q[b, h])
+    Hq, Hkv = q.shape[1], k.shape[1]
+    hk = h // (Hq // Hkv)
+    rows = np.asarray(list(rows), dtype=np.int64)
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    if causal and q.shape[2] != k.shape[2]:
+        raise ValueError("causal attention is defined here for Lq == Lk only")
+    return _head_attention(q_bh[rows], _as64(k[b, hk]), _as64(v[b, hk]), scale,
+                           causal, row_ids=rows)
+
+
+def attention_decode(q, k_cache, v_cache, seqlens, scale: Optional[float] = None,
+                     threads: Optional[int] = None, batches: Optional[Sequence[int]] = None):
+    """One query token per sequence against a KV cache.
+
+    q [B,Hq,d]; k_cache, v_cache [B,Hkv,Lmax,d]; seqlens [B] integers.
+    Sequence b sees cache slots 0..min(seqlens[b], Lmax)-1.
+    Returns O [B,Hq,d] and LSE [B,Hq] (rows of batches not listed stay 0).
+    """
+    q = _as64(q)
+    B, Hq, d = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    if Hkv == 0 or Hq % Hkv != 0:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    if scale is None:
+        scale = default_scale(d)
+    group = Hq // Hkv
+    lens = [max(0, min(int(x), Lmax)) for x in np.asarray(seqlens).reshape(-1)]
+    if batches is None:
+        batches = range(B)
+    o = np.zeros((B, Hq, v_cache.shape[3]))
+    lse = np.zeros((B, Hq))
+    items = [(b, hk) for b in batches for hk in range(Hkv)]
+
+    def one(item):
+        b, hk = item
+        L = lens[b]
+        kk = _as64(k_cache[b, hk, :L])
+        vv = _as64(v_cache[b, hk, :L])
+        qq = q[b, hk * group:(hk + 1) * group]
+        return _head_attention(qq, kk, vv, scale, causal=False)
+
+    results = _pool_map(one, items, threads)
+    for (b, hk), (ob, lb) in zip(items, results):
+        o[b, hk * group:(hk + 1) * group] = ob
+        lse[b, hk * group:(hk + 1) * group] = lb
+    return o, lse
+
+
+def merge_partials(o_parts, lse_parts):
+    """Combine attention results computed over disjoint key subsets.
+
+    o_parts [S, ..., d] holds each part's normalised output, lse_parts [S, ...]
+    each part's log-sum-exp.  This is the normaliser identity of the cnblogs
+    page's section 四 (rescale each block's exponent sum by exp(m_block - m)
+    and add), applied to whole parts: with M = max_s LSE_s,
+      LSE = M + ln sum_s exp(LSE_s - M),  O = sum_s exp(LSE_s - LSE) O_s.
+    Parts with LSE = -inf carry no keys and get weight 0.  Works in the dtype
+    it is given.
+    """
+    o_parts = np.asarray(o_parts)
+    lse_parts = np.asarray(lse_parts)
+    M = lse_parts.max(axis=0)
+    empty = ~np.isfinite(M)
+    M_safe = np.where(empty, 0.0, M).astype(lse_parts.dtype)
+    w = np.exp(lse_parts - M_safe[None])
+    tot = w.sum(axis=0)
+    tot_safe = np.where(empty, 1.0, tot).astype(lse_parts.dtype)
+    with np.errstate(divide="ignore"):
+        lse = np.where(empty, -np.inf, M_safe + np.log(tot_safe)).astype(lse_parts.dtype)
+    o = (w[..., None] * o_parts).sum(axis=0) / tot_safe[..., None]
+    o = np.where(empty[..., None], 0.0, o).astype(o_parts.dtype)
+    return o, lse
+
+
+def softmax_two_blocks(x: np.ndarray):
+    """Row softmax of x [..., n] from two key blocks' own statistics.
+
+    The cnblogs page's section 四 derivation: each block keeps its own maximum
+    m_i and exponent sum e_i; the global maximum is m = max(m_1, m_2), the
+    normaliser is e_1 exp(m_1 - m) + e_2 exp(m_2 - m), and each block's
+    weights are exp(x - m) / l.  Computed in x's dtype.
+    """
+    n = x.shape[-1]
+    mid = n // 2
+    x1, x2 = x[..., :mid], x[..., mid:]
+    m1 = x1.max(axis=-1, keepdims=True)
+    m2 = x2.max(axis=-1, keepdims=True)
+    m = np.maximum(m1, m2)
+    e1 = np.exp(x1 - m1).sum(axis=-1, keepdims=True)
+    e2 = np.exp(x2 - m2).sum(axis=-1, keepdims=True)
+    l = e1 * np.exp(m1 - m) + e2 * np.exp(m2 - m)
+    return np.concatenate([np.exp(x1 - m) / l, np.exp(x2 - m) / l], axis=-1)
+
+
+def brute_force_attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
+                          n_keys: Optional[Sequence[int]] = None):
+    """Per-element pure-Python evaluation for tiny shapes (no numpy arithmetic).
+
+    q [B][Hq][Lq][d], k and v [B][Hkv][Lk][d] as nested sequences; n_keys
+    optionally limits the keys seen by batch b (decode lengths).  Every score
+    is a math.fsum of products; every row is normalised with math.fsum.
+    Returns nested lists O [B][Hq][Lq][d] and LSE [B][Hq][Lq].
+    """
+    B, Hq = len(q), len(q[0])
+    Hkv = len(k[0])
+    d = len(q[0][0][0])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    group = Hq // Hkv
+    O, LSE = [], []
+    for b in range(B):
+        Ob, Lb = [], []
+        for h in range(Hq):
+            hk = h // group
+            keys = k[b][hk]
+            vals = v[b][hk]
+            nk = len(keys) if n_keys is None else min(int(n_keys[b]), len(keys))
+            Oh, Lh = [], []
+            for i, qi in enumerate(q[b][h]):
+                visible = [j for j in range(nk) if not (causal and j > i)]
+                if not visible:
+                    Oh.append([0.0] * len(vals[0]) if vals else [])
+                    Lh.append(-math.inf)
+                    continue
+                s = {j: math.fsum(float(qi[t]) * float(keys[j][t]) for t in range(d)) * scale
+                     for j in visible}
+                m = max(s.values())
+                e = {j: math.exp(s[j] - m) for j in visible}
+                l = math.fsum(e.values())
+                Oh.append([math.fsum(e[j] * float(vals[j][c]) for j in visible) / l
+                           for c in range(len(vals[0]))])
+                Lh.append(m + math.log(l))
+            Ob.append(Oh)
+            Lb.append(Lh)
+        O.append(Ob)
+        LSE.append(Lb)
+    return O, LSE

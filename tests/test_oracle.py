@@ -1,0 +1,341 @@
+"""Pins on the CPU oracle: facts fixed by the pages and by mathematics, not by
+the oracle itself.  No GPU needed.
+
+Each test names the part of the oracle a plausible slip would break (a dropped
+term, a wrong sign or index, a transposed operand); test_planted_mistakes
+checks that the pins do catch such slips.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sdpa_oracle as orc
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")
+
+
+def rnd(shape, seed, mul=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * mul
+
+
+# ---------------------------------------------------------------- P-1 softmax
+@pytest.mark.parametrize("causal", [False, True])
+def test_prob_rows_sum_to_one(causal):
+    q, k, v = rnd((2, 3, 17, 8), 1), rnd((2, 3, 17, 8), 2), rnd((2, 3, 17, 8), 3)
+    _, _, s, p = orc.attention_forward(q, k, v, causal=causal, return_sp=True)
+    assert np.abs(p.sum(-1) - 1.0).max() <= 1e-13
+    assert (p >= 0).all()
+    if causal:
+        iu = np.triu_indices(17, 1)
+        assert (p[..., iu[0], iu[1]] == 0).all()
+        assert np.isneginf(s[..., iu[0], iu[1]]).all()
+
+
+# ------------------------------------------------------ P-2 constant V rows
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_values_return_the_constant(causal):
+    q, k = rnd((1, 2, 23, 16), 4, 3.0), rnd((1, 2, 23, 16), 5)
+    c = rnd((16,), 6)
+    v = np.broadcast_to(c, (1, 2, 23, 16)).copy()
+    o, _ = orc.attention_forward(q, k, v, causal=causal)
+    assert np.abs(o - c).max() <= 1e-13
+
+
+# ------------------------------------------------------- P-3 causal row 0
+def test_causal_first_row_is_first_value():
+    q, k, v = rnd((1, 1, 9, 8), 7), rnd((1, 1, 9, 8), 8), rnd((1, 1, 9, 8), 9)
+    o, lse = orc.attention_forward(q, k, v, causal=True)
+    assert np.abs(o[0, 0, 0] - v[0, 0, 0]).max() <= 1e-15
+    s00 = float(np.dot(q[0, 0, 0], k[0, 0, 0])) / math.sqrt(8)
+    assert abs(lse[0, 0, 0] - s00) <= 1e-14
+
+
+# --------------------------------------------------- P-4 brute force (fsum)
+@pytest.mark.parametrize("causal,Hq,Hkv,n,d", [
+    (False, 2, 2, 5, 4), (True, 2, 2, 7, 8), (False, 4, 2, 6, 8), (True, 4, 1, 16, 8),
+    (False, 3, 3, 1, 4), (True, 2, 1, 3, 2)])
+def test_matches_brute_force(causal, Hq, Hkv, n, d):
+    B = 2
+    q, k, v = rnd((B, Hq, n, d), 10, 2.0), rnd((B, Hkv, n, d), 11), rnd((B, Hkv, n, d), 12)
+    o, lse = orc.attention_forward(q, k, v, causal=causal)
+    ob, lb = orc.brute_force_attention(q.tolist(), k.tolist(), v.tolist(), causal=causal)
+    ob, lb = np.array(ob), np.array(lb)
+    assert np.abs(o - ob).max() <= 1e-12 * max(1.0, np.abs(ob).max())
+    assert np.abs(lse - lb).max() <= 1e-12 * max(1.0, np.abs(lb).max())
+
+
+def test_decode_matches_brute_force():
+    B, Hq, Hkv, L, d = 3, 4, 2, 9, 8
+    q, k, v = rnd((B, Hq, d), 13), rnd((B, Hkv, L, d), 14), rnd((B, Hkv, L, d), 15)
+    lens = [9, 1, 4]
+    o, lse = orc.attention_decode(q, k, v, lens)
+    ob, lb = orc.brute_force_attention(q[:, :, None, :].tolist(), k.tolist(), v.tolist(),
+                                       n_keys=lens)
+    assert np.abs(o - np.array(ob)[:, :, 0]).max() <= 1e-12
+    assert np.abs(lse - np.array(lb)[:, :, 0]).max() <= 1e-12
+
+
+# ------------------------------------------- P-5 zero queries: uniform rows
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_queries_give_uniform_weights(causal):
+    n = 13
+    q = np.zeros((1, 1, n, 8))
+    k, v = rnd((1, 1, n, 8), 16), rnd((1, 1, n, 8), 17)
+    o, lse = orc.attention_forward(q, k, v, causal=causal)
+    for i in range(n):
+        vis = i + 1 if causal else n
+        assert np.abs(o[0, 0, i] - v[0, 0, :vis].mean(0)).max() <= 1e-14
+        assert abs(lse[0, 0, i] - math.log(vis)) <= 1e-14
+
+
+# ----------------------------------- P-6 shifting every key by one vector
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_shift_moves_only_lse(causal):
+    n, d = 11, 8
+    q, k, v = rnd((1, 2, n, d), 18), rnd((1, 2, n, d), 19), rnd((1, 2, n, d), 20)
+    u = rnd((d,), 21)
+    o1, l1 = orc.attention_forward(q, k, v, causal=causal)
+    o2, l2 = orc.attention_forward(q, k + u, v, causal=causal)
+    assert np.abs(o1 - o2).max() <= 1e-12
+    expect = l1 + (q @ u) / math.sqrt(d)
+    assert np.abs(l2 - expect).max() <= 1e-12
+
+
+# ---------------------------------- P-7 joint permutation of keys and values
+def test_key_value_permutation_invariance():
+    n, d = 19, 8
+    q, k, v = rnd((2, 2, 7, d), 22), rnd((2, 2, n, d), 23), rnd((2, 2, n, d), 24)
+    perm = np.random.default_rng(25).permutation(n)
+    o1, l1 = orc.attention_forward(q, k, v)
+    o2, l2 = orc.attention_forward(q, k[:, :, perm], v[:, :, perm])
+    assert np.abs(o1 - o2).max() <= 1e-13 and np.abs(l1 - l2).max() <= 1e-13
+    # A single key row moved without its value row must change the result.
+    k3 = k.copy()
+    k3[:, :, [0, 1]] = k3[:, :, [1, 0]]
+    o3, _ = orc.attention_forward(q, k3, v)
+    assert np.abs(o1 - o3).max() > 1e-3
+
+
+# ----------------------------------------------- P-8 grouped-query heads
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_equals_expanded_mha(causal):
+    B, Hq, Hkv, n, d = 2, 8, 2, 10, 8
+    q, k, v = rnd((B, Hq, n, d), 26), rnd((B, Hkv, n, d), 27), rnd((B, Hkv, n, d), 28)
+    o1, l1 = orc.attention_forward(q, k, v, causal=causal)
+    kx = torch.from_numpy(k).repeat_interleave(Hq // Hkv, dim=1).numpy()
+    vx = torch.from_numpy(v).repeat_interleave(Hq // Hkv, dim=1).numpy()
+    o2, l2 = orc.attention_forward(q, kx, vx, causal=causal)
+    assert np.abs(o1 - o2).max() == 0 and np.abs(l1 - l2).max() == 0
+    # and head 1 must not read kv head 1 (the h % Hkv slip)
+    o3, _ = orc.attention_forward(q[:, 1:2], k[:, 1:2], v[:, 1:2], causal=causal)
+    assert np.abs(o1[:, 1:2] - o3).max() > 1e-3
+
+
+# ------------------------------- P-9 decode = last row of causal prefill
+def test_decode_is_last_row_of_causal_prefill():
+    B, Hq, Hkv, Lmax, d = 3, 4, 2, 12, 8
+    kc, vc = rnd((B, Hkv, Lmax, d), 29), rnd((B, Hkv, Lmax, d), 30)
+    qfull = rnd((B, Hq, Lmax, d), 31)
+    lens = [12, 5, 1]
+    qd = np.stack([qfull[b, :, lens[b] - 1] for b in range(B)])
+    o, lse = orc.attention_decode(qd, kc, vc, lens)
+    for b, L in enumerate(lens):
+        op, lp = orc.attention_forward(qfull[b:b + 1, :, :L], kc[b:b + 1, :, :L],
+                                       vc[b:b + 1, :, :L], causal=True)
+        assert np.abs(o[b] - op[0, :, L - 1]).max() <= 1e-13
+        assert np.abs(lse[b] - lp[0, :, L - 1]).max() <= 1e-13
+
+
+def test_decode_clamps_and_empty():
+    B, Hq, Hkv, Lmax, d = 2, 2, 1, 6, 4
+    q, kc, vc = rnd((B, Hq, d), 32), rnd((B, Hkv, Lmax, d), 33), rnd((B, Hkv, Lmax, d), 34)
+    o, lse = orc.attention_decode(q, kc, vc, [0, 100])
+    assert (o[0] == 0).all() and np.isneginf(lse[0]).all()
+    o6, l6 = orc.attention_decode(q, kc, vc, [0, 6])
+    assert np.array_equal(o[1], o6[1]) and np.array_equal(lse[1], l6[1])
+
+
+# ------------------------------------------- P-10 block / part merging
+@pytest.mark.parametrize("cuts", [[5], [1, 2, 30], [16, 17], [0, 40]])
+def test_merge_of_key_parts_equals_whole(cuts):
+    n, d = 40, 8
+    q, k, v = rnd((1, 3, 6, d), 35, 2.0), rnd((1, 3, n, d), 36), rnd((1, 3, n, d), 37)
+    o, lse = orc.attention_forward(q, k, v)
+    bounds = [0] + list(cuts) + [n]
+    parts = [orc.attention_forward(q, k[:, :, a:b], v[:, :, a:b]) for a, b in zip(bounds, bounds[1:])]
+    om, lm = orc.merge_partials([p[0] for p in parts], [p[1] for p in parts])
+    assert np.abs(om - o).max() <= 1e-14 and np.abs(lm - lse).max() <= 1e-13
+
+
+def test_merge_all_empty_parts():
+    o, l = orc.merge_partials(np.zeros((3, 2, 4)), np.full((3, 2), -np.inf))
+    assert (o == 0).all() and np.isneginf(l).all()
+
+
+def test_two_block_softmax_page_demo():
+    """The online-softmax demo: randn(2, 512, 4096) * 2 split into two key
+    blocks; the page expects agreement near machine precision (1e-6) in fp32."""
+    fig = json.load(open(GOLDEN))["online_softmax_demo"]
+    x = torch.randn(*fig["shape"], generator=torch.Generator().manual_seed(0)) * fig["x_scale"]
+    x32 = x.numpy()
+    ref32 = torch.softmax(x, dim=-1).numpy()
+    got32 = orc.softmax_two_blocks(x32)
+    assert got32.dtype == np.float32
+    assert np.abs(got32 - ref32).max() <= 10 * fig["max_abs_diff_fp32_order"]
+    x64 = x32.astype(np.float64)
+    ref64 = np.exp(x64 - x64.max(-1, keepdims=True))
+    ref64 /= ref64.sum(-1, keepdims=True)
+    assert np.abs(orc.softmax_two_blocks(x64) - ref64).max() <= 1e-15
+
+
+# ------------------------------------------ P-11 large score magnitudes
+def test_large_scores_stay_finite_and_pick_the_max():
+    n, d = 9, 8
+    q, k, v = rnd((1, 1, n, d), 38, 100.0), rnd((1, 1, n, d), 39), rnd((1, 1, n, d), 40)
+    o, lse, s, _ = orc.attention_forward(q, k, v, return_sp=True)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    for i in range(n):
+        row = s[0, 0, i]
+        j = int(np.argmax(row))
+        assert np.abs(row).max() > 100  # far outside exp's float range unless shifted
+        # |O - V_j| <= sum_{j' != j} e^(s_j' - s_j) |V_j' - V_j|, and
+        # 0 <= LSE - s_j = ln(1 + sum_{j' != j} e^(s_j' - s_j)) <= that sum.
+        w = np.exp(np.delete(row, j) - row[j])
+        dv = np.abs(np.delete(v[0, 0], j, axis=0) - v[0, 0, j]).max(-1)
+        assert np.abs(o[0, 0, i] - v[0, 0, j]).max() <= (w * dv).sum() + 1e-12
+        assert -1e-12 <= lse[0, 0, i] - row[j] <= w.sum() + 1e-12
+
+
+# ------------------------------------------------------------ P-12 n = 1
+def test_single_key():
+    q, k, v = rnd((2, 2, 1, 8), 41), rnd((2, 2, 1, 8), 42), rnd((2, 2, 1, 8), 43)
+    for causal in (False, True):
+        o, lse = orc.attention_forward(q, k, v, causal=causal)
+        assert np.abs(o - v).max() <= 1e-15
+        s = (q * k).sum(-1) / math.sqrt(8)
+        assert np.abs(lse - s).max() <= 1e-14
+
+
+def test_no_keys():
+    q = rnd((1, 1, 3, 4), 44)
+    o, lse = orc.attention_forward(q, np.zeros((1, 1, 0, 4)), np.zeros((1, 1, 0, 4)))
+    assert (o == 0).all() and np.isneginf(lse).all()
+
+
+# ------------------------------------------------ P-13 independent library
+@pytest.mark.parametrize("causal,Hq,Hkv", [(False, 4, 4), (True, 4, 4), (True, 8, 2)])
+def test_matches_torch_sdpa_float64(causal, Hq, Hkv):
+    B, n, d = 2, 33, 16
+    q, k, v = rnd((B, Hq, n, d), 45, 2.0), rnd((B, Hkv, n, d), 46), rnd((B, Hkv, n, d), 47)
+    o, lse, s, _ = orc.attention_forward(q, k, v, causal=causal, return_sp=True)
+    tq = torch.from_numpy(q)
+    tk = torch.from_numpy(k).repeat_interleave(Hq // Hkv, 1)
+    tv = torch.from_numpy(v).repeat_interleave(Hq // Hkv, 1)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal).numpy()
+    assert np.abs(o - ref).max() <= 1e-12
+    ref_lse = torch.logsumexp(torch.from_numpy(s), dim=-1).numpy()
+    assert np.abs(lse - ref_lse).max() <= 1e-12
+
+
+def test_explicit_scale():
+    q, k, v = rnd((1, 2, 7, 8), 48), rnd((1, 2, 7, 8), 49), rnd((1, 2, 7, 8), 50)
+    o, _ = orc.attention_forward(q, k, v, scale=0.3)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), scale=0.3).numpy()
+    assert np.abs(o - ref).max() <= 1e-12
+
+
+# --------------------------------------- sampled rows = the same definition
+def test_rows_helper_agrees_with_full():
+    q, k, v = rnd((2, 4, 30, 8), 51), rnd((2, 2, 30, 8), 52), rnd((2, 2, 30, 8), 53)
+    o, lse = orc.attention_forward(q, k, v, causal=True)
+    rows = [0, 7, 29]
+    orow, lrow = orc.attention_forward_rows(q, k, v, 1, 3, rows, causal=True)
+    assert np.array_equal(orow, o[1, 3, rows]) and np.array_equal(lrow, lse[1, 3, rows])
+
+
+def test_threaded_equals_serial():
+    q, k, v = rnd((2, 6, 20, 8), 54), rnd((2, 3, 20, 8), 55), rnd((2, 3, 20, 8), 56)
+    a = orc.attention_forward(q, k, v, causal=True, threads=1)
+    b = orc.attention_forward(q, k, v, causal=True, threads=4)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ------------------------------------------ page figures for the accounting
+def test_accounting_matches_page_figures():
+    fig = json.load(open(GOLDEN))
+    MB, GB, KB = 2 ** 20, 2 ** 30, 2 ** 10
+    assert wl.score_matrix_bytes(4096) / MB == fig["score_matrix_fp32_n4096_MB"]["value"]
+    tot = wl.score_matrix_bytes(4096) * 96 * 40 / GB
+    assert abs(tot - fig["score_matrix_fp32_n4096_h96_l40_GB"]["value"]) <= \
+        fig["score_matrix_fp32_n4096_h96_l40_GB"]["tolerance_rel"] * tot
+    assert 2 * wl.score_matrix_bytes(4096) / MB == fig["score_plus_prob_fp32_n4096_MB"]["value"]
+    # Q, K, V, O + LSE for one head in fp32; Q/K/V alone is the page's 3.0 MB
+    qkv = wl.algorithmic_bytes_fwd(1, 1, 1, 4096, 4096, 64, 4) - 4096 * 64 * 4 - 4096 * 4
+    assert qkv / MB == fig["qkv_fp32_n4096_d64_one_head_MB"]["value"]
+    assert 2 * 4096 * 4 / KB == fig["row_stats_fp32_n4096_KB"]["value"]
+    assert 2 * wl.score_matrix_bytes(4096) // (2 * 4096 * 4) == fig["stats_saving_ratio_n4096"]["value"]
+
+
+def test_workload_flop_counts():
+    assert wl.algorithmic_flops_fwd(1, 96, 4096, 4096, 64, False) == 412_316_860_416
+    assert wl.algorithmic_flops_fwd(4, 16, 2048, 2048, 80, True) == 42_949_672_960
+    assert wl.algorithmic_flops_fwd(1, 32, 8192, 8192, 128, True) == 549_755_813_888
+
+
+def test_input_recipe_is_bf16_round_to_nearest_even():
+    """The bf16 inputs are torch's RNE rounding of the float32 draws; check it
+    against a bit-level round-to-nearest-even written out here."""
+    x = torch.randn(200_000, generator=torch.Generator().manual_seed(3)) * 3
+    bits = x.view(torch.int32).numpy().astype(np.int64) & 0xFFFFFFFF
+    lsb = (bits >> 16) & 1
+    rounded = ((bits + 0x7FFF + lsb) >> 16) & 0xFFFF
+    got = x.to(torch.bfloat16).view(torch.int16).numpy().astype(np.int64) & 0xFFFF
+    assert np.array_equal(rounded, got)
+
+
+# -------------------------------------------- planted mistakes are caught
+def _mutant(kind):
+    """Copies of the oracle's per-head step with one plausible slip each."""
+    def f(q, k, v, scale, causal, row_ids=None, n_keys=None, return_sp=False):
+        if kind == "scale_1_over_d":
+            scale = scale * scale
+        s = (q @ k.T) * scale
+        if kind == "transposed" and s.shape[0] == s.shape[1]:
+            s = s.T.copy()
+        n_rows, lk = s.shape
+        rid = np.arange(n_rows) if row_ids is None else row_ids
+        if causal:
+            off = 1 if kind == "mask_off_by_one" else 0
+            s = np.where(np.arange(lk)[None, :] > rid[:, None] + off, -np.inf, s)
+        m = s.max(-1)
+        e = np.exp(s - m[:, None])
+        l = e.sum(-1)
+        p = e / l[:, None]
+        o = (p @ v) if kind != "unnormalised" else (e @ v)
+        lse = m + np.log(l) if kind != "lse_drops_max" else np.log(l)
+        if return_sp:
+            return o, lse, s, p
+        return o, lse
+    return f
+
+
+@pytest.mark.parametrize("kind", ["scale_1_over_d", "transposed", "mask_off_by_one",
+                                  "unnormalised", "lse_drops_max"])
+def test_planted_mistakes(monkeypatch, kind):
+    monkeypatch.setattr(orc, "_head_attention", _mutant(kind))
+    failures = 0
+    for fn in (lambda: test_matches_torch_sdpa_float64(True, 4, 4),
+               lambda: test_causal_first_row_is_first_value(),
+               lambda: test_key_shift_moves_only_lse(True),
+               lambda: test_constant_values_return_the_constant(False)):
+        try:
+            fn()
+        except AssertionError:
+            failures += 1
+    assert failures >= 1, f"planted mistake {kind} not caught"

@@ -1,0 +1,159 @@
+"""Seeded synthetic inputs for the attention forward and decode workloads.
+
+This module only draws numbers and fixes shapes.  It holds none of the
+attention arithmetic, so both the CPU oracle (through the tests) and the GPU
+path (through the tests and the benchmark) can consume the very same bits.
+
+Recipe (one per workload):
+  g = torch.Generator().manual_seed(seed)
+  Q, K, V = randn(shape, generator=g) in float32, drawn in that order
+  bf16 workloads: each tensor rounded to bfloat16 (round-to-nearest-even,
+                  torch's own conversion); the oracle receives exactly those
+                  values widened to float64
+  decode workloads, after V: lengths = randint(lo, hi + 1, (B,), generator=g)
+
+The five named workloads are the shapes the attention pages discuss:
+the GPT-3-scale layer (B=1, 96 heads, n=4096, d=64) from "Flash Attention原理"
+section 一, the d=80 head size that needed padding on other hardware from
+"SDPA backend 与 FlashAttention" section 9, n=8k prefill with grouped KV heads
+from the same page's section 12, and batched decode against a KV cache from its
+section 5.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+from typing import Optional
+
+import torch
+
+
+@dataclass(frozen=True)
+class FwdWorkload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Lq: int
+    Lk: int
+    d: int
+    dtype: str          # "bf16" or "f32"
+    causal: bool
+    seed: int
+
+    @property
+    def group(self) -> int:
+        return self.Hq // self.Hkv
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Lmax: int
+    d: int
+    len_lo: int
+    len_hi: int          # inclusive
+    dtype: str
+    seed: int
+
+    @property
+    def group(self) -> int:
+        return self.Hq // self.Hkv
+
+
+# The five workloads, smallest first.
+C1 = FwdWorkload("fwd_f32_b1_h2_n256_d64", 1, 2, 2, 256, 256, 64, "f32", False, 1001)
+C2 = FwdWorkload("fwd_bf16_b1_h96_n4096_d64", 1, 96, 96, 4096, 4096, 64, "bf16", False, 1002)
+C3 = FwdWorkload("fwd_bf16_causal_b4_h16_n2048_d80", 4, 16, 16, 2048, 2048, 80, "bf16", True, 1003)
+C4 = FwdWorkload("fwd_bf16_causal_gqa_b1_hq32_hkv8_n8192_d128", 1, 32, 8, 8192, 8192, 128, "bf16", True, 1004)
+C5 = DecodeWorkload("decode_bf16_gqa_b64_hq32_hkv8_lmax8192_d128", 64, 32, 8, 8192, 128, 1024, 8192, "bf16", 1005)
+
+FWD_WORKLOADS = {w.name: w for w in (C1, C2, C3, C4)}
+DECODE_WORKLOADS = {C5.name: C5}
+
+
+def torch_dtype(name: str) -> torch.dtype:
+    return {"bf16": torch.bfloat16, "f32": torch.float32}[name]
+
+
+def make_fwd_inputs(w: FwdWorkload, q_mul: float = 1.0):
+    """Q [B,Hq,Lq,d], K and V [B,Hkv,Lk,d] on the CPU in the workload's dtype.
+
+    q_mul scales Q before rounding; values above 1 give peaky score rows whose
+    running maximum moves from tile to tile.
+    """
+    g = torch.Generator().manual_seed(w.seed)
+    q = torch.randn((w.B, w.Hq, w.Lq, w.d), generator=g, dtype=torch.float32)
+    k = torch.randn((w.B, w.Hkv, w.Lk, w.d), generator=g, dtype=torch.float32)
+    v = torch.randn((w.B, w.Hkv, w.Lk, w.d), generator=g, dtype=torch.float32)
+    if q_mul != 1.0:
+        q = q * q_mul
+    dt = torch_dtype(w.dtype)
+    return q.to(dt), k.to(dt), v.to(dt)
+
+
+def make_decode_inputs(w: DecodeWorkload, poison_tail: bool = False,
+                       lengths: Optional[torch.Tensor] = None):
+    """q [B,Hq,d]; k_cache and v_cache [B,Hkv,Lmax,d]; seqlens int32 [B].
+
+    With poison_tail, every cache slot at or beyond a sequence's length holds
+    NaN, so any read of it would show up in the output.
+    """
+    g = torch.Generator().manual_seed(w.seed)
+    q = torch.randn((w.B, w.Hq, w.d), generator=g, dtype=torch.float32)
+    k = torch.randn((w.B, w.Hkv, w.Lmax, w.d), generator=g, dtype=torch.float32)
+    v = torch.randn((w.B, w.Hkv, w.Lmax, w.d), generator=g, dtype=torch.float32)
+    lens = torch.randint(w.len_lo, w.len_hi + 1, (w.B,), generator=g, dtype=torch.int32)
+    if lengths is not None:
+        lens = lengths.to(torch.int32).clone()
+    dt = torch_dtype(w.dtype)
+    q, k, v = q.to(dt), k.to(dt), v.to(dt)
+    if poison_tail:
+        for b in range(w.B):
+            L = int(lens[b])
+            k[b, :, L:, :] = float("nan")
+            v[b, :, L:, :] = float("nan")
+    return q, k, v, lens
+
+
+def shrink(w, **kw):
+    """A copy of a workload with some sizes replaced (name and seed kept unless given)."""
+    return replace(w, **kw)
+
+
+# ---------------------------------------------------------------------------
+# Work and traffic accounting (counts from shapes; no attention arithmetic).
+
+def algorithmic_flops_fwd(B, Hq, Lq, Lk, d, causal) -> int:
+    """4 * Lq * Lk * d per (batch, query head): Q K^T and P V are 2 * Lq * Lk * d
+    each.  Causal work is credited as exactly half; padding is never credited."""
+    f = 4 * B * Hq * Lq * Lk * d
+    return f // 2 if causal else f
+
+
+def algorithmic_bytes_fwd(B, Hq, Hkv, Lq, Lk, d, elem_bytes) -> int:
+    """Q, K, V read once and O written once in the input dtype, LSE once in fp32.
+
+    Q/K/V are the traffic that cannot be avoided ("Flash Attention原理", section
+    六); S and P never leave the chip.
+    """
+    return (B * Hq * Lq * d * 2 + B * Hkv * Lk * d * 2) * elem_bytes + B * Hq * Lq * 4
+
+
+def algorithmic_flops_decode(seqlens, Hq, d, Lmax) -> int:
+    tot = sum(max(0, min(int(x), Lmax)) for x in seqlens)
+    return 4 * tot * Hq * d
+
+
+def algorithmic_bytes_decode(seqlens, Hq, Hkv, d, elem_bytes, Lmax) -> int:
+    """Valid K and V cache rows read once, Q read and O written once, LSE in fp32."""
+    lens = [max(0, min(int(x), Lmax)) for x in seqlens]
+    B = len(lens)
+    return sum(lens) * Hkv * d * 2 * elem_bytes + B * Hq * d * 2 * elem_bytes + B * Hq * 4
+
+
+def score_matrix_bytes(n: int, elem_bytes: int = 4) -> int:
+    """Bytes of one materialised n x n score (or probability) matrix."""
+    return n * n * elem_bytes
