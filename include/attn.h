@@ -1,0 +1,167 @@
+/*
+ * attn.h - fused scaled dot-product attention forward for AMD Instinct MI355X
+ * (gfx950): prefill and single-token decode against a KV cache.
+ *
+ * What is computed (per batch b and query head h, with key/value head
+ * hk = h / (Hq / Hkv)):
+ *
+ *     S   = Q[b,h] K[b,hk]^T * scale           scores, one row per query
+ *     S[i,j] = -inf where j > i                 only when causal
+ *     P   = softmax(S) along the key axis       after subtracting the row max
+ *     O   = P V[b,hk]
+ *     LSE = m + ln(l) per row                   m = row max, l = sum exp(S - m)
+ *
+ * This is the attention of "Flash Attention原理：分块计算与重计算" (cnblogs),
+ * section 一 (shapes (batch, num_heads, seq_len, head_dim), P = softmax(S /
+ * sqrt(d)) over keys, O = P V, default scale head_dim^-1/2), with the step
+ * order Q K^T, scale, causal mask, softmax, times V of "PyTorch Profiler 實戰：
+ * 五種 Attention 實現的 GPU 核心剖析" ("核心概念").  The library computes it
+ * tile by tile with the online softmax of the cnblogs page's section 四, so
+ * S and P never reach device memory; only O and the per-row statistics (the
+ * m and l of its section 五, returned as one log-sum-exp) are written.
+ * Grouped-query heads (several query heads sharing one key/value head) follow
+ * "SDPA backend 与 FlashAttention", sections 11-12.  Decode (one query token
+ * against the cached keys and values, the inference case of the cnblogs FAQ
+ * Q12-Q13 and "SDPA backend 与 FlashAttention" section 5) splits each
+ * sequence's keys into chunks and merges the partial results with the same
+ * section 四 rescaling identity applied to (O, LSE) pairs.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library allocates nothing and keeps no state between calls; the entry
+ *     points are thread-safe.
+ *   - Sizes and strides are int64 element counts.  The innermost (head_dim)
+ *     stride is 1 for every tensor.  Every base pointer must be 16-byte
+ *     aligned and every non-innermost stride a multiple of 16 bytes (8 bf16
+ *     or 4 fp32 elements), so that each row starts on a 16-byte boundary.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *     Work is enqueued and the call returns; the status reports argument
+ *     validation and kernel launch only (an execution fault surfaces at the
+ *     caller's next synchronisation).
+ *   - Invalid or unsupported arguments are rejected with an error status
+ *     before anything is enqueued.  Nothing falls back to another method.
+ *   - Outputs must not overlap inputs.  Inputs are assumed finite.
+ *   - Arithmetic: bf16 inputs are multiplied on bf16 matrix cores with fp32
+ *     accumulation; the softmax runs in fp32; probabilities are rounded to
+ *     bf16 (round-to-nearest-even) before the P V product; O is rounded to
+ *     the input dtype (round-to-nearest-even).  fp32 inputs stay in fp32
+ *     throughout.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_BF16 = 0, /* bfloat16 Q/K/V/O */
+  ATTN_F32 = 1   /* float32 Q/K/V/O */
+} attn_dtype_t;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,       /* negative size, Hkv == 0 with work to do, Hq % Hkv != 0,
+                               causal with Lq != Lk */
+  ATTN_ERR_DTYPE = 3,       /* dtype not one of attn_dtype_t */
+  ATTN_ERR_LAYOUT = 4,      /* misaligned base pointer, stride not a multiple of
+                               16 bytes, or negative stride */
+  ATTN_ERR_UNSUPPORTED = 5, /* valid arguments with no kernel (head_dim, dtype or
+                               group size outside the supported set) */
+  ATTN_ERR_WORKSPACE = 6,   /* decode workspace NULL or smaller than required */
+  ATTN_ERR_HIP = 7          /* the HIP runtime refused the launch */
+} attn_status_t;
+
+/* Prefill: every query row attends to the keys of its (batch, kv head). */
+typedef struct {
+  const void *q;   /* [B, Hq,  Lq, d] */
+  const void *k;   /* [B, Hkv, Lk, d] */
+  const void *v;   /* [B, Hkv, Lk, d] */
+  void *o;         /* [B, Hq,  Lq, d], same dtype as q */
+  float *lse;      /* [B, Hq, Lq] fp32, contiguous; natural-log log-sum-exp of
+                      the scaled (and masked) score row */
+  int64_t B, Hq, Hkv, Lq, Lk, d;
+  int64_t q_strides[3]; /* element strides of (batch, head, token); d stride is 1 */
+  int64_t k_strides[3];
+  int64_t v_strides[3];
+  int64_t o_strides[3];
+  int32_t dtype;   /* attn_dtype_t */
+  int32_t causal;  /* nonzero: query i sees keys j <= i (top-left; needs Lq == Lk) */
+  float scale;     /* multiplier of Q K^T; 0 selects 1/sqrt(d) */
+} attn_fwd_args_t;
+
+/* Decode: one query token per sequence against a ragged KV cache. */
+typedef struct {
+  const void *q;          /* [B, Hq, d] */
+  const void *k_cache;    /* [B, Hkv, Lmax, d]; slots >= seqlens[b] are never read */
+  const void *v_cache;    /* [B, Hkv, Lmax, d] */
+  const int32_t *seqlens; /* device int32 [B]; sequence b sees slots 0..seqlens[b]-1.
+                             Values are clamped to [0, Lmax]; a sequence of length
+                             0 yields O = 0 and LSE = -inf. */
+  void *o;                /* [B, Hq, d], same dtype as q */
+  float *lse;             /* [B, Hq] fp32, contiguous */
+  int64_t B, Hq, Hkv, Lmax, d;
+  int64_t q_strides[2];   /* (batch, head) */
+  int64_t k_strides[3];   /* (batch, head, token) */
+  int64_t v_strides[3];
+  int64_t o_strides[2];
+  int32_t dtype;          /* attn_dtype_t; decode supports ATTN_BF16 */
+  float scale;            /* 0 selects 1/sqrt(d) */
+} attn_decode_args_t;
+
+/*
+ * attn_fwd - prefill attention forward, one kernel launch.
+ * Supported: dtype bf16 or f32; d in {64, 80, 128}; Hq % Hkv == 0; causal
+ * needs Lq == Lk.  Any size may be 0: then nothing is launched (Lk == 0 with
+ * Lq > 0 writes O = 0 and LSE = -inf).  Returns ATTN_OK or the first error
+ * found; on error nothing is enqueued.
+ */
+attn_status_t attn_fwd(const attn_fwd_args_t *args, void *stream);
+
+/*
+ * attn_decode_workspace_bytes - bytes of device workspace attn_decode needs
+ * for these sizes (fp32 partial outputs and log-sum-exps of every key chunk).
+ * Returns 0 for invalid sizes.
+ */
+size_t attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Lmax, int64_t d);
+
+/*
+ * attn_decode - split-KV decode: one kernel computes a partial (O, LSE) per
+ * (sequence, kv head, key chunk), a second merges the chunks of each query
+ * head.  `workspace` is caller-owned device memory of at least
+ * attn_decode_workspace_bytes(B, Hq, Lmax, d) bytes, 256-byte aligned; its
+ * contents on entry do not matter and are overwritten.  Calls that share a
+ * workspace must be ordered on one stream.
+ * Supported: dtype bf16; d in {64, 128}; Hq % Hkv == 0.  The query heads of
+ * one kv head are served 16 at a time, so a group larger than 16 reads its
+ * keys and values once per 16 query heads.  B == 0 or Hq == 0 is a no-op;
+ * Lmax == 0 writes O = 0 and LSE = -inf.  Exactly two kernels are enqueued
+ * (one when Lmax == 0).
+ */
+attn_status_t attn_decode(const attn_decode_args_t *args, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/* Argument checks only (no device work, no HIP call): the status attn_fwd /
+ * attn_decode would return before launching.  Usable without a GPU. */
+attn_status_t attn_validate_fwd(const attn_fwd_args_t *args);
+attn_status_t attn_validate_decode(const attn_decode_args_t *args);
+
+/* Static, human-readable name of a status code. */
+const char *attn_status_str(attn_status_t status);
+
+/* Static name of the kernel attn_fwd would launch for these arguments, or
+ * "none" if they are invalid or unsupported.  No device work. */
+const char *attn_kernel_name(const attn_fwd_args_t *args);
+
+/* Library version string. */
+const char *attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

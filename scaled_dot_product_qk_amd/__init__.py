@@ -1,0 +1,235 @@
+"""Python binding of the gfx950 attention library (argument marshalling only).
+
+Every step of the computation runs in the HIP kernels of libattn_gfx950.so;
+this module only fills the C structs of include/attn.h from torch tensors and
+calls the C entry points with the same names.  torch provides device memory
+and the current stream.  There is no other execution path: if the library is
+missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn_gfx950.so")
+
+ATTN_BF16, ATTN_F32 = 0, 1
+STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_DTYPE",
+                4: "ATTN_ERR_LAYOUT", 5: "ATTN_ERR_UNSUPPORTED", 6: "ATTN_ERR_WORKSPACE",
+                7: "ATTN_ERR_HIP"}
+EXPORTED = ("attn_fwd", "attn_decode", "attn_decode_workspace_bytes", "attn_validate_fwd",
+            "attn_validate_decode", "attn_status_str", "attn_kernel_name", "attn_version")
+
+_i64 = ctypes.c_int64
+_i64x3 = _i64 * 3
+_i64x2 = _i64 * 2
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("B", _i64), ("Hq", _i64), ("Hkv", _i64), ("Lq", _i64), ("Lk", _i64), ("d", _i64),
+                ("q_strides", _i64x3), ("k_strides", _i64x3), ("v_strides", _i64x3),
+                ("o_strides", _i64x3),
+                ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+                ("seqlens", ctypes.c_void_p), ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("B", _i64), ("Hq", _i64), ("Hkv", _i64), ("Lmax", _i64), ("d", _i64),
+                ("q_strides", _i64x2), ("k_strides", _i64x3), ("v_strides", _i64x3),
+                ("o_strides", _i64x2),
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({status_str(status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (built by scaled_dot_product_qk_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m scaled_dot_product_qk_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.attn_fwd.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
+        L.attn_fwd.restype = ctypes.c_int
+        L.attn_validate_fwd.argtypes = [ctypes.POINTER(FwdArgs)]
+        L.attn_validate_fwd.restype = ctypes.c_int
+        L.attn_kernel_name.argtypes = [ctypes.POINTER(FwdArgs)]
+        L.attn_kernel_name.restype = ctypes.c_char_p
+        L.attn_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p]
+        L.attn_decode.restype = ctypes.c_int
+        L.attn_validate_decode.argtypes = [ctypes.POINTER(DecodeArgs)]
+        L.attn_validate_decode.restype = ctypes.c_int
+        L.attn_decode_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
+        L.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_status_str.argtypes = [ctypes.c_int]
+        L.attn_status_str.restype = ctypes.c_char_p
+        L.attn_version.argtypes = []
+        L.attn_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().attn_status_str(status).decode()
+
+
+def version() -> str:
+    return lib().attn_version().decode()
+
+
+# ------------------------------------------------------------------ helpers
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    return -1
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def make_fwd_args(q, k, v, o, lse, causal: bool, scale: Optional[float]) -> FwdArgs:
+    a = FwdArgs()
+    a.q, a.k, a.v, a.o, a.lse = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr()
+    a.B, a.Hq, a.Lq, a.d = q.shape
+    a.Hkv, a.Lk = k.shape[1], k.shape[2]
+    a.q_strides = _i64x3(*q.stride()[:3])
+    a.k_strides = _i64x3(*k.stride()[:3])
+    a.v_strides = _i64x3(*v.stride()[:3])
+    a.o_strides = _i64x3(*o.stride()[:3])
+    a.dtype = _dtype_code(q)
+    a.causal = 1 if causal else 0
+    a.scale = 0.0 if scale is None else float(scale)
+    return a
+
+
+def _check_device(*tensors):
+    dev = tensors[0].device
+    for t in tensors:
+        if t.device.type != "cuda" or t.device != dev:
+            raise ValueError("all tensors must live on the same GPU device")
+
+
+def _check_fwd_tensors(q, k, v):
+    _check_device(q, k, v)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, d]")
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    for t in (q, k, v):
+        if t.numel() and t.stride(3) != 1:
+            raise ValueError("head_dim must be the innermost, contiguous dimension")
+
+
+# ------------------------------------------------------------------ entry points
+def attn_fwd(q, k, v, causal: bool = False, scale: Optional[float] = None, out=None, lse=None,
+             stream=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """O and LSE of attention over device tensors q [B,Hq,Lq,d], k/v [B,Hkv,Lk,d]."""
+    import torch
+    _check_fwd_tensors(q, k, v)
+    B, Hq, Lq, d = q.shape
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    _check_device(q, out, lse)
+    if not lse.is_contiguous() or lse.dtype != torch.float32 or lse.shape != (B, Hq, Lq):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Lq] tensor")
+    if out.shape != q.shape or out.dtype != q.dtype or (out.numel() and out.stride(3) != 1):
+        raise ValueError("out must match q's shape and dtype with a contiguous head_dim")
+    args = make_fwd_args(q, k, v, out, lse, causal, scale)
+    st = lib().attn_fwd(ctypes.byref(args), _stream_handle(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd")
+    return out, lse
+
+
+def kernel_name(q, k, v, causal: bool = False, scale: Optional[float] = None) -> str:
+    """Name of the kernel attn_fwd launches for these tensors ("none" if invalid)."""
+    args = make_fwd_args(q, k, v, q, q, causal, scale)
+    return lib().attn_kernel_name(ctypes.byref(args)).decode()
+
+
+def attn_decode_workspace_bytes(B: int, Hq: int, Lmax: int, d: int) -> int:
+    return int(lib().attn_decode_workspace_bytes(B, Hq, Lmax, d))
+
+
+def make_decode_args(q, k_cache, v_cache, seqlens, o, lse, scale: Optional[float]) -> DecodeArgs:
+    a = DecodeArgs()
+    a.q, a.k_cache, a.v_cache = q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr()
+    a.seqlens, a.o, a.lse = seqlens.data_ptr(), o.data_ptr(), lse.data_ptr()
+    a.B, a.Hq, a.d = q.shape
+    a.Hkv, a.Lmax = k_cache.shape[1], k_cache.shape[2]
+    a.q_strides = _i64x2(*q.stride()[:2])
+    a.k_strides = _i64x3(*k_cache.stride()[:3])
+    a.v_strides = _i64x3(*v_cache.stride()[:3])
+    a.o_strides = _i64x2(*o.stride()[:2])
+    a.dtype = _dtype_code(q)
+    a.scale = 0.0 if scale is None else float(scale)
+    return a
+
+
+def attn_decode(q, k_cache, v_cache, seqlens, scale: Optional[float] = None, workspace=None,
+                out=None, lse=None, stream=None):
+    """O [B,Hq,d] and LSE [B,Hq] of one query token per sequence against a KV cache.
+
+    q [B,Hq,d]; k_cache/v_cache [B,Hkv,Lmax,d]; seqlens int32 [B] on the device.
+    workspace: optional uint8 device tensor of attn_decode_workspace_bytes bytes.
+    """
+    import torch
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [B,Hq,d] and the caches [B,Hkv,Lmax,d]")
+    if seqlens.dtype != torch.int32 or seqlens.numel() != q.shape[0]:
+        raise ValueError("seqlens must be int32 [B]")
+    for t in (q, k_cache, v_cache):
+        if t.numel() and t.stride(-1) != 1:
+            raise ValueError("head_dim must be the innermost, contiguous dimension")
+    _check_device(q, k_cache, v_cache, seqlens)
+    B, Hq, d = q.shape
+    Lmax = k_cache.shape[2]
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check_device(q, out, lse)
+    if not lse.is_contiguous() or lse.dtype != torch.float32 or lse.shape != (B, Hq):
+        raise ValueError("lse must be a contiguous float32 [B, Hq] tensor")
+    if out.shape != q.shape or out.dtype != q.dtype or (out.numel() and out.stride(-1) != 1):
+        raise ValueError("out must match q's shape and dtype with a contiguous head_dim")
+    need = attn_decode_workspace_bytes(B, Hq, Lmax, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_device(q, workspace)
+    args = make_decode_args(q, k_cache, v_cache, seqlens, out, lse, scale)
+    st = lib().attn_decode(ctypes.byref(args), workspace.data_ptr(), workspace.numel(),
+                           _stream_handle(stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode")
+    return out, lse
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)

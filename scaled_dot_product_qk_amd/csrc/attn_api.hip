@@ -1,0 +1,249 @@
+// Host side of the attention library: the C ABI declared in include/attn.h.
+// Validates arguments on the host, picks the kernel instance for (dtype,
+// head_dim, causal), sizes the grid and launches on the caller's stream.  No
+// allocation, no state, no fallback: anything without a kernel is an error.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "attn.h"
+#include "decode.h"
+#include "fwd_bf16.h"
+#include "fwd_f32.h"
+
+using namespace attn_dev;
+
+namespace {
+
+constexpr int64_t kI32Max = std::numeric_limits<int32_t>::max();
+constexpr int64_t kGridYMax = 65535;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Element strides of every non-innermost dimension must keep rows 16-byte
+// aligned and be non-negative.
+bool strides_ok(const int64_t* s, int n, int elem_bytes) {
+  const int64_t unit = 16 / elem_bytes;
+  for (int i = 0; i < n; ++i)
+    if (s[i] < 0 || s[i] % unit != 0) return false;
+  return true;
+}
+
+bool fwd_head_dim_supported(int64_t d) { return d == 64 || d == 80 || d == 128; }
+bool decode_head_dim_supported(int64_t d) { return d == 64 || d == 128; }
+
+int elem_bytes_of(int32_t dtype) { return dtype == ATTN_F32 ? 4 : 2; }
+
+float effective_scale(float scale, int64_t d) {
+  return scale == 0.f ? 1.0f / std::sqrt((float)d) : scale;
+}
+
+int64_t decode_chunks(int64_t Lmax) { return (Lmax + kDecChunk - 1) / kDecChunk; }
+
+}  // namespace
+
+extern "C" attn_status_t attn_validate_fwd(const attn_fwd_args_t* a) {
+  if (!a) return ATTN_ERR_NULL;
+  if (a->dtype != ATTN_BF16 && a->dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+  if (a->B < 0 || a->Hq < 0 || a->Hkv < 0 || a->Lq < 0 || a->Lk < 0 || a->d < 0)
+    return ATTN_ERR_SHAPE;
+  if (!std::isfinite(a->scale)) return ATTN_ERR_SHAPE;
+  if (!fwd_head_dim_supported(a->d)) return ATTN_ERR_UNSUPPORTED;
+  const bool work = a->B > 0 && a->Hq > 0 && a->Lq > 0;
+  if (a->Hq > 0 && (a->Hkv == 0 || a->Hq % a->Hkv != 0)) return ATTN_ERR_SHAPE;
+  if (a->causal && a->Lq != a->Lk) return ATTN_ERR_SHAPE;
+  if (!work) return ATTN_OK;
+  if (!a->q || !a->o || !a->lse) return ATTN_ERR_NULL;
+  if (a->Lk > 0 && (!a->k || !a->v)) return ATTN_ERR_NULL;
+  const int eb = elem_bytes_of(a->dtype);
+  if (!aligned16(a->q) || !aligned16(a->o) || !aligned16(a->lse)) return ATTN_ERR_LAYOUT;
+  if (a->Lk > 0 && (!aligned16(a->k) || !aligned16(a->v))) return ATTN_ERR_LAYOUT;
+  if (!strides_ok(a->q_strides, 3, eb) || !strides_ok(a->o_strides, 3, eb) ||
+      !strides_ok(a->k_strides, 3, eb) || !strides_ok(a->v_strides, 3, eb))
+    return ATTN_ERR_LAYOUT;
+  // Index ranges the kernels keep in 32 bits, and the grid limits.
+  if (a->Lq > kI32Max || a->Lk > kI32Max || a->B * a->Hq > kI32Max) return ATTN_ERR_UNSUPPORTED;
+  if ((a->Lq + 127) / 128 > kGridYMax) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+extern "C" const char* attn_kernel_name(const attn_fwd_args_t* a) {
+  if (attn_validate_fwd(a) != ATTN_OK) return "none";
+  const bool bf = a->dtype == ATTN_BF16;
+  const bool c = a->causal != 0;
+  switch (a->d) {
+    case 64: return bf ? (c ? "attn_fwd_bf16_d64_causal" : "attn_fwd_bf16_d64")
+                       : (c ? "attn_fwd_f32_d64_causal" : "attn_fwd_f32_d64");
+    case 80: return bf ? (c ? "attn_fwd_bf16_d80_causal" : "attn_fwd_bf16_d80")
+                       : (c ? "attn_fwd_f32_d80_causal" : "attn_fwd_f32_d80");
+    case 128: return bf ? (c ? "attn_fwd_bf16_d128_causal" : "attn_fwd_bf16_d128")
+                        : (c ? "attn_fwd_f32_d128_causal" : "attn_fwd_f32_d128");
+    default: return "none";
+  }
+}
+
+static attn_status_t launch_status() {
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+template <int D, bool CAUSAL>
+static attn_status_t launch_fwd_bf16(const FwdParams& p, int grid_x, hipStream_t s) {
+  constexpr int lds = Bf16FwdShape<D>::kLdsBytes;
+  auto kern = attn_fwd_bf16_kernel<D, CAUSAL>;
+  static bool attr_set = false;  // racing first calls set the same value
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=
+        hipSuccess)
+      return ATTN_ERR_HIP;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(grid_x, p.n_qtiles), dim3(256), lds, s, p);
+  return launch_status();
+}
+
+template <int D, bool CAUSAL>
+static attn_status_t launch_fwd_f32(const FwdParams& p, int grid_x, hipStream_t s) {
+  constexpr int lds = F32FwdShape<D>::kLdsBytes;
+  auto kern = attn_fwd_f32_kernel<D, CAUSAL>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=
+        hipSuccess)
+      return ATTN_ERR_HIP;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(grid_x, (p.Lq + 127) / 128), dim3(256), lds, s, p);
+  return launch_status();
+}
+
+extern "C" attn_status_t attn_fwd(const attn_fwd_args_t* a, void* stream) {
+  const attn_status_t st = attn_validate_fwd(a);
+  if (st != ATTN_OK) return st;
+  if (a->B == 0 || a->Hq == 0 || a->Lq == 0) return ATTN_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  FwdParams p;
+  p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->o; p.lse = a->lse;
+  p.q_sb = a->q_strides[0]; p.q_sh = a->q_strides[1]; p.q_st = a->q_strides[2];
+  p.k_sb = a->k_strides[0]; p.k_sh = a->k_strides[1]; p.k_st = a->k_strides[2];
+  p.v_sb = a->v_strides[0]; p.v_sh = a->v_strides[1]; p.v_st = a->v_strides[2];
+  p.o_sb = a->o_strides[0]; p.o_sh = a->o_strides[1]; p.o_st = a->o_strides[2];
+  p.Hq = (int)a->Hq;
+  p.group = (int)(a->Hq / a->Hkv);
+  p.Lq = (int)a->Lq;
+  p.Lk = (int)a->Lk;
+  p.n_qtiles = (int)((a->Lq + 127) / 128);
+  p.scale_log2 = effective_scale(a->scale, a->d) * kLog2e;
+  const int grid_x = (int)(a->B * a->Hq);
+  const bool c = a->causal != 0;
+
+  if (a->dtype == ATTN_BF16) {
+    switch (a->d) {
+      case 64: return c ? launch_fwd_bf16<64, true>(p, grid_x, s) : launch_fwd_bf16<64, false>(p, grid_x, s);
+      case 80: return c ? launch_fwd_bf16<80, true>(p, grid_x, s) : launch_fwd_bf16<80, false>(p, grid_x, s);
+      case 128: return c ? launch_fwd_bf16<128, true>(p, grid_x, s) : launch_fwd_bf16<128, false>(p, grid_x, s);
+    }
+  } else {
+    switch (a->d) {
+      case 64: return c ? launch_fwd_f32<64, true>(p, grid_x, s) : launch_fwd_f32<64, false>(p, grid_x, s);
+      case 80: return c ? launch_fwd_f32<80, true>(p, grid_x, s) : launch_fwd_f32<80, false>(p, grid_x, s);
+      case 128: return c ? launch_fwd_f32<128, true>(p, grid_x, s) : launch_fwd_f32<128, false>(p, grid_x, s);
+    }
+  }
+  return ATTN_ERR_UNSUPPORTED;
+}
+
+extern "C" size_t attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Lmax, int64_t d) {
+  if (B < 0 || Hq < 0 || Lmax < 0 || d <= 0) return 0;
+  const int64_t rows = B * Hq * decode_chunks(Lmax);
+  const int64_t obytes = (rows * d * 4 + 255) / 256 * 256;
+  return (size_t)(obytes + rows * 4);
+}
+
+extern "C" attn_status_t attn_validate_decode(const attn_decode_args_t* a) {
+  if (!a) return ATTN_ERR_NULL;
+  if (a->dtype != ATTN_BF16 && a->dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+  if (a->B < 0 || a->Hq < 0 || a->Hkv < 0 || a->Lmax < 0 || a->d < 0) return ATTN_ERR_SHAPE;
+  if (!std::isfinite(a->scale)) return ATTN_ERR_SHAPE;
+  if (a->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!decode_head_dim_supported(a->d)) return ATTN_ERR_UNSUPPORTED;
+  if (a->Hq > 0 && (a->Hkv == 0 || a->Hq % a->Hkv != 0)) return ATTN_ERR_SHAPE;
+  if (a->B == 0 || a->Hq == 0) return ATTN_OK;
+  if (!a->q || !a->o || !a->lse || !a->seqlens) return ATTN_ERR_NULL;
+  if (a->Lmax > 0 && (!a->k_cache || !a->v_cache)) return ATTN_ERR_NULL;
+  if (!aligned16(a->q) || !aligned16(a->o) || !aligned16(a->lse)) return ATTN_ERR_LAYOUT;
+  if (a->Lmax > 0 && (!aligned16(a->k_cache) || !aligned16(a->v_cache))) return ATTN_ERR_LAYOUT;
+  if ((reinterpret_cast<uintptr_t>(a->seqlens) & 3u) != 0) return ATTN_ERR_LAYOUT;
+  if (!strides_ok(a->q_strides, 2, 2) || !strides_ok(a->o_strides, 2, 2) ||
+      !strides_ok(a->k_strides, 3, 2) || !strides_ok(a->v_strides, 3, 2))
+    return ATTN_ERR_LAYOUT;
+  if (a->Lmax > kI32Max || a->B > kGridYMax || a->B * a->Hq > kI32Max) return ATTN_ERR_UNSUPPORTED;
+  const int64_t hgroups = (a->Hq / a->Hkv + kDecHeadsPerGroup - 1) / kDecHeadsPerGroup;
+  if (a->Hkv * hgroups > kGridYMax) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+template <int D>
+static attn_status_t launch_decode(const DecodeParams& p, int B, hipStream_t s) {
+  if (p.n_chunks > 0) {
+    hipLaunchKernelGGL(attn_decode_split_kernel<D>, dim3(p.n_chunks, p.Hkv * p.n_hgroups, B),
+                       dim3(256), 0, s, p);
+    if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
+  }
+  hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3(B * p.Hq), dim3(D), 0, s, p);
+  return launch_status();
+}
+
+extern "C" attn_status_t attn_decode(const attn_decode_args_t* a, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  const attn_status_t st = attn_validate_decode(a);
+  if (st != ATTN_OK) return st;
+  if (a->B == 0 || a->Hq == 0) return ATTN_OK;
+  const size_t need = attn_decode_workspace_bytes(a->B, a->Hq, a->Lmax, a->d);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_LAYOUT;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  DecodeParams p;
+  p.q = a->q; p.k = a->k_cache; p.v = a->v_cache; p.seqlens = a->seqlens;
+  const int64_t rows = a->B * a->Hq * decode_chunks(a->Lmax);
+  p.o_part = reinterpret_cast<float*>(workspace);
+  p.lse_part = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                        (rows * a->d * 4 + 255) / 256 * 256);
+  p.o = a->o; p.lse = a->lse;
+  p.q_sb = a->q_strides[0]; p.q_sh = a->q_strides[1];
+  p.k_sb = a->k_strides[0]; p.k_sh = a->k_strides[1]; p.k_st = a->k_strides[2];
+  p.v_sb = a->v_strides[0]; p.v_sh = a->v_strides[1]; p.v_st = a->v_strides[2];
+  p.o_sb = a->o_strides[0]; p.o_sh = a->o_strides[1];
+  p.Hq = (int)a->Hq;
+  p.Hkv = (int)a->Hkv;
+  p.group = (int)(a->Hq / a->Hkv);
+  p.Lmax = (int)a->Lmax;
+  p.n_chunks = (int)decode_chunks(a->Lmax);
+  p.n_hgroups = (p.group + kDecHeadsPerGroup - 1) / kDecHeadsPerGroup;
+  p.scale_log2 = effective_scale(a->scale, a->d) * kLog2e;
+  switch (a->d) {
+    case 64: return launch_decode<64>(p, (int)a->B, s);
+    case 128: return launch_decode<128>(p, (int)a->B, s);
+  }
+  return ATTN_ERR_UNSUPPORTED;
+}
+
+extern "C" const char* attn_status_str(attn_status_t s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "null pointer";
+    case ATTN_ERR_SHAPE: return "invalid shape or argument";
+    case ATTN_ERR_DTYPE: return "invalid dtype";
+    case ATTN_ERR_LAYOUT: return "misaligned pointer or stride";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+extern "C" const char* attn_version(void) { return "attn-gfx950 0.1.0"; }
+

@@ -1,0 +1,241 @@
+// Split-KV decode for gfx950: one query token per sequence against a ragged
+// bf16 KV cache, then a merge of the per-chunk partial results.
+//
+// Decode is the inference case of "Flash Attention原理：分块计算与重计算"
+// (cnblogs) FAQ Q12-Q13: each new token's query attends to the keys and values
+// already in the cache.  "SDPA backend 与 FlashAttention" section 5 notes that
+// its bottleneck differs from prefill: here the cache is streamed from HBM
+// once and the arithmetic per byte is tiny, so the kernel is built for
+// bandwidth.
+//
+// Split kernel: one workgroup per (sequence b, kv head, chunk of 512 cache
+// slots, group of up to 16 query heads sharing that kv head).  Its 4 waves take
+// 128 slots each and walk them 32 keys at a time with the tiled online softmax
+// of the cnblogs page's sections 三-四; the 4 partial results are combined in
+// LDS and one (O_s, LSE_s) pair per query head is written to the workspace.
+// Chunks at or beyond a sequence's length exit at once; slots at or beyond the
+// length are never loaded.
+//
+// Matrix-core use: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with the 16 keys on
+// the M side and the query heads of the group on the N side; O^T = V^T P^T on
+// the same instruction.  K arrives from HBM already in the A-operand layout
+// (16 keys x 16-byte slices).  V^T is built in registers: each lane loads 8
+// cache rows of 8 consecutive head_dim values (4 full rows per load
+// instruction) and transposes them with byte permutes, so O^T row m of the
+// product number t is head_dim index 8m + t.  No LDS is used on the way.
+//
+// Merge kernel: one workgroup per (b, query head) combines the chunks with the
+// cnblogs section 四 identity on (O_s, LSE_s) pairs:
+//   M = max_s LSE_s,  LSE = M + ln sum_s e^(LSE_s - M),
+//   O = sum_s e^(LSE_s - LSE) O_s.
+#pragma once
+
+#include "device_common.h"
+
+namespace attn_dev {
+
+constexpr int kDecChunk = 512;                 // cache slots per split workgroup
+constexpr int kDecWaves = 4;
+constexpr int kDecWaveSlots = kDecChunk / kDecWaves;
+constexpr int kDecHeadsPerGroup = 16;
+
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* seqlens;
+  float* o_part;    // [B, Hq, n_chunks, D]
+  float* lse_part;  // [B, Hq, n_chunks]
+  void* o;          // merge output [B, Hq, D] (strided)
+  float* lse;       // [B, Hq]
+  int64_t q_sb, q_sh;
+  int64_t k_sb, k_sh, k_st;
+  int64_t v_sb, v_sh, v_st;
+  int64_t o_sb, o_sh;
+  int Hq, Hkv, group, Lmax, n_chunks, n_hgroups;
+  float scale_log2;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeParams p) {
+  static_assert(D % 32 == 0 && D <= 128, "decode head_dim must be 32, 64, 96 or 128");
+  constexpr int KC = D / 32;      // k-slices of S^T = K Q^T
+  __shared__ float red_m[kDecWaves][16];
+  __shared__ float red_l[kDecWaves][16];
+  __shared__ float red_o[kDecWaves][16][D + 1];
+
+  const int chunk = blockIdx.x;
+  const int hkv = blockIdx.y / p.n_hgroups;
+  const int hg = blockIdx.y - hkv * p.n_hgroups;
+  const int b = blockIdx.z;
+  int L = p.seqlens[b];
+  L = L < 0 ? 0 : (L > p.Lmax ? p.Lmax : L);
+  const int c0 = chunk * kDecChunk;
+  if (c0 >= L) return;  // whole workgroup leaves together
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 15;   // query column / A-operand row
+  const int g = lane >> 4;   // 16-lane row
+
+  const int hidx = kDecHeadsPerGroup * hg + n;  // head within the kv group
+  const bool hvalid = hidx < p.group;
+  const int h = hkv * p.group + hidx;
+
+  // Q^T B operand: k slot (g, i) of slice kc is head_dim index 8*(4*kc + g) + i.
+  u32x4 qop[KC];
+  {
+    const uint16_t* qr = reinterpret_cast<const uint16_t*>(p.q) + b * p.q_sb + (int64_t)h * p.q_sh;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) qop[kc] = hvalid ? load16(qr + 8 * (4 * kc + g)) : zero16();
+  }
+
+  const uint16_t* kg = reinterpret_cast<const uint16_t*>(p.k) + b * p.k_sb + hkv * p.k_sh;
+  const uint16_t* vg = reinterpret_cast<const uint16_t*>(p.v) + b * p.v_sb + hkv * p.v_sh;
+
+  const int w0 = c0 + wave * kDecWaveSlots;
+  const int w1 = min(w0 + kDecWaveSlots, L);
+
+  f32x4 oacc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) oacc[t][r] = 0.f;
+  float m_run = kNegInf, l_run = 0.f;
+
+  for (int base = w0; base < w1; base += 32) {
+    u32x4 kreg[2][KC];
+    u32x4 vreg[8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = base + 16 * kb + n;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        kreg[kb][kc] = key < w1 ? load16(kg + (int64_t)key * p.k_st + 8 * (4 * kc + g)) : zero16();
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int key = base + 16 * (i >> 2) + 4 * g + (i & 3);
+      vreg[i] = (key < w1 && 8 * n < D) ? load16(vg + (int64_t)key * p.v_st + 8 * n) : zero16();
+    }
+
+    // S^T (16 keys x 16 query columns) for the two 16-key blocks.
+    f32x4 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[kb][r] = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) s[kb] = mfma16(kreg[kb][kc], qop[kc], s[kb]);
+    }
+
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = base + 16 * kb + 4 * g + r;
+        const float x = key < w1 ? s[kb][r] * p.scale_log2 : kNegInf;
+        s[kb][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = max_xor32(max_xor16(mx));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s[kb][r] = fast_exp2(s[kb][r] - m_new);
+        rs += s[kb][r];
+      }
+    l_run = l_run * alpha + rs;
+    // P^T B operand: k slot (g, i) is key base + 16*(i/4) + 4*g + i%4.
+    u32x4 pop;
+    pop[0] = pack_bf16x2(s[0][0], s[0][1]);
+    pop[1] = pack_bf16x2(s[0][2], s[0][3]);
+    pop[2] = pack_bf16x2(s[1][0], s[1][1]);
+    pop[3] = pack_bf16x2(s[1][2], s[1][3]);
+
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) oacc[t][r] *= alpha;
+      // A operand of product t: lane row n is head_dim 8n + t, k slot (g, i)
+      // the key of vreg[i]; element t of each loaded row, paired by key.
+      u32x4 a;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = vreg[2 * j][t >> 1], hi = vreg[2 * j + 1][t >> 1];
+        a[j] = (t & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+      }
+      oacc[t] = mfma16(a, pop, oacc[t]);
+    }
+  }
+
+  // Combine the 4 waves' partial results in LDS.
+  const float l_wave = sum_xor32(sum_xor16(l_run));
+  if (g == 0) {
+    red_m[wave][n] = m_run;
+    red_l[wave][n] = l_wave;
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int d = 8 * (4 * g + r) + t;
+      if (d < D) red_o[wave][n][d] = oacc[t][r];
+    }
+  __syncthreads();
+
+  const int64_t part_row0 = ((int64_t)b * p.Hq + hkv * p.group + kDecHeadsPerGroup * hg) * p.n_chunks;
+  for (int idx = tid; idx < 16 * D; idx += 256) {
+    const int col = idx / D;
+    const int d = idx - col * D;
+    if (kDecHeadsPerGroup * hg + col >= p.group) continue;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, red_m[w][col]);
+    float lsum = 0.f, acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float wt = fast_exp2(red_m[w][col] - M);  // empty wave: exp2(-inf) = 0
+      lsum += wt * red_l[w][col];
+      acc += wt * red_o[w][col][d];
+    }
+    const int64_t row = part_row0 + (int64_t)col * p.n_chunks + chunk;
+    p.o_part[row * D + d] = acc / lsum;
+    if (d == 0) p.lse_part[row] = (M + log2f(lsum)) * kLn2;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void attn_decode_merge_kernel(DecodeParams p) {
+  const int bh = blockIdx.x;
+  const int b = bh / p.Hq;
+  const int h = bh - b * p.Hq;
+  const int d = threadIdx.x;
+  int L = p.seqlens[b];
+  L = L < 0 ? 0 : (L > p.Lmax ? p.Lmax : L);
+  const int ns = (L + kDecChunk - 1) / kDecChunk;
+  const int64_t row0 = (int64_t)bh * p.n_chunks;
+
+  float M = kNegInf;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, p.lse_part[row0 + s]);
+  float wsum = 0.f, acc = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float w = expf(p.lse_part[row0 + s] - M);
+    wsum += w;
+    acc += w * p.o_part[(row0 + s) * D + d];
+  }
+  const float o = ns > 0 ? acc / wsum : 0.f;
+  uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + b * p.o_sb + (int64_t)h * p.o_sh;
+  // bf16 round-to-nearest-even of one value.
+  orow[d] = (uint16_t)(pack_bf16x2(o, 0.f) & 0xffffu);
+  if (d == 0) p.lse[bh] = ns > 0 ? M + logf(wsum) : kNegInf;
+}
+
+}  // namespace attn_dev

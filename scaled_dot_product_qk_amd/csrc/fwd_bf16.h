@@ -1,0 +1,319 @@
+// Prefill attention forward, bf16 inputs, for gfx950.
+//
+// Method: the tiled forward with online softmax of "Flash Attention原理：分块
+// 计算与重计算" (cnblogs), sections 三-五.  Q is split into row tiles, K and V
+// into key tiles; for every key tile the kernel forms the score tile, updates
+// each row's running maximum m and normaliser l, rescales the partial output by
+// exp(m_old - m_new) (section 四) and adds P V.  Only O and the row statistics
+// (returned as LSE = m + ln l, section 五) are written.
+//
+// Work decomposition: one workgroup of 4 waves per (batch, query head, tile
+// of 128 query rows); wave w owns 32 rows.  Key/value tiles of 64 keys are
+// staged in LDS, double buffered, and shared by the 4 waves.
+//
+// Orientation: every product is taken transposed, S^T = K Q^T and
+// O^T = V^T P^T, so that in both the score accumulator and the output
+// accumulator a lane holds one query's values (lane % 32 = query).  Then
+//   * the row max and row sum are in-lane reductions plus one exchange with
+//     lane ^ 32 (the other half of the keys);
+//   * the probabilities leave the score accumulator already in the B-operand
+//     layout of the P V product (no LDS round trip);
+//   * the rescale of the output by exp(m_old - m_new) is a per-lane scalar.
+// The key order inside each 16-key slice of the P V contraction is permuted to
+// match the score accumulator's row order; V^T is written to LDS in that
+// permuted order so each lane's 8 keys are one 16-byte read.
+//
+// Causal (top-left, Lq == Lk): key tiles entirely above a wave's last row are
+// skipped; tiles that straddle the diagonal or the end of the keys are masked
+// to -inf before the max.  Key tile 0 is processed first and always holds a
+// visible key for every row, so the running max is finite from the first tile
+// on and exp(-inf - m) = 0 never meets exp(-inf - (-inf)).
+#pragma once
+
+#include "device_common.h"
+
+namespace attn_dev {
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t q_sb, q_sh, q_st;
+  int64_t k_sb, k_sh, k_st;
+  int64_t v_sb, v_sh, v_st;
+  int64_t o_sb, o_sh, o_st;
+  int Hq;
+  int group;  // Hq / Hkv
+  int Lq;
+  int Lk;
+  int n_qtiles;
+  float scale_log2;  // scale * log2(e)
+};
+
+template <int D>
+struct Bf16FwdShape {
+  static constexpr int kWaves = 4;
+  static constexpr int kBR = 32 * kWaves;        // query rows per workgroup
+  static constexpr int kBC = 64;                 // keys per tile
+  static constexpr int kKC = D / 16;             // k-slices of the Q K^T product
+  static constexpr int kDP = (D + 31) / 32 * 32; // rows of O^T padded to 32
+  static constexpr int kND = kDP / 32;           // 32-row blocks of O^T
+  static constexpr int kChunks = D / 8;          // 16-byte chunks per row
+  static constexpr int kKPitch = D + 8;          // K row pitch in LDS (elements)
+  static constexpr int kVPitch = kBC + 8;        // V^T row pitch in LDS (elements)
+  static constexpr int kKElems = kBC * kKPitch;
+  static constexpr int kVElems = kDP * kVPitch;
+  static constexpr int kBufElems = kKElems + kVElems;
+  static constexpr int kLdsBytes = 2 * kBufElems * 2;
+  static constexpr int kKItems = kBC * kChunks;         // 16-byte K loads per tile
+  static constexpr int kVItems = (kBC / 2) * kChunks;   // (key pair, chunk) V loads
+  static constexpr int kKIter = (kKItems + 255) / 256;
+  static constexpr int kVIter = (kVItems + 255) / 256;
+  static_assert(D % 16 == 0, "head_dim must be a multiple of 16");
+};
+
+// Position of key kk (0..15) of a 16-key slice inside V^T's LDS row: the
+// score accumulator gives lane half g the keys {4g..4g+3, 8+4g..8+4g+3} of a
+// slice, stored contiguously at 8g..8g+7.
+__device__ __forceinline__ int vt_pos16(int kk) {
+  return ((kk >> 2) & 1) * 8 + (kk >> 3) * 4 + (kk & 3);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdParams p) {
+  using S = Bf16FwdShape<D>;
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lq = lane & 31;  // query row within the wave (n index)
+  const int g = lane >> 5;   // lane half
+
+  const int bh = blockIdx.x;
+  const int b = bh / p.Hq;
+  const int h = bh - b * p.Hq;
+  const int hk = h / p.group;
+  const int qt = CAUSAL ? (p.n_qtiles - 1 - (int)blockIdx.y) : (int)blockIdx.y;
+  const int q0 = qt * S::kBR;
+  const int qrow = q0 + wave * 32 + lq;
+
+  const uint16_t* qg = reinterpret_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh;
+  const uint16_t* kg = reinterpret_cast<const uint16_t*>(p.k) + b * p.k_sb + hk * p.k_sh;
+  const uint16_t* vg = reinterpret_cast<const uint16_t*>(p.v) + b * p.v_sb + hk * p.v_sh;
+
+  // Q^T as the B operand of S^T = K Q^T: lane holds Q[qrow][16*kc + 8*g .. +8].
+  u32x4 qop[S::kKC];
+  {
+    const bool ok = qrow < p.Lq;
+    const uint16_t* qr = qg + (int64_t)qrow * p.q_st + 8 * g;
+#pragma unroll
+    for (int kc = 0; kc < S::kKC; ++kc) qop[kc] = ok ? load16(qr + 16 * kc) : zero16();
+  }
+
+  // Key tiles this workgroup visits.
+  int kv_end = p.Lk;
+  if (CAUSAL) kv_end = min(kv_end, q0 + S::kBR);
+  const int n_tiles = (kv_end + S::kBC - 1) / S::kBC;
+  const int wave_last_row = q0 + wave * 32 + 31;
+
+  // Zero the padded rows of V^T (head_dim not a multiple of 32) once; the
+  // loader never writes them and their products land in discarded O^T rows.
+  if (S::kDP != D) {
+    for (int i = tid; i < (S::kDP - D) * S::kVPitch; i += 256) {
+      lds[S::kKElems + D * S::kVPitch + i] = 0;
+      lds[S::kBufElems + S::kKElems + D * S::kVPitch + i] = 0;
+    }
+  }
+
+  // ---- global -> register staging of one key tile ----
+  u32x4 kreg[S::kKIter];
+  u32x4 vreg[S::kVIter][2];
+
+  auto load_tile = [&](int t) {
+    const int kv0 = t * S::kBC;
+#pragma unroll
+    for (int it = 0; it < S::kKIter; ++it) {
+      const int item = tid + 256 * it;
+      const int row = item / S::kChunks;
+      const int ch = item - row * S::kChunks;
+      const bool ok = (item < S::kKItems) && (kv0 + row < p.Lk);
+      kreg[it] = ok ? load16(kg + (int64_t)(kv0 + row) * p.k_st + 8 * ch) : zero16();
+    }
+#pragma unroll
+    for (int it = 0; it < S::kVIter; ++it) {
+      const int item = tid + 256 * it;
+      const int pr = item / S::kChunks;  // key pair
+      const int ch = item - pr * S::kChunks;
+      const bool in = item < S::kVItems;
+      const int key = kv0 + 2 * pr;
+      vreg[it][0] = (in && key < p.Lk) ? load16(vg + (int64_t)key * p.v_st + 8 * ch) : zero16();
+      vreg[it][1] = (in && key + 1 < p.Lk) ? load16(vg + (int64_t)(key + 1) * p.v_st + 8 * ch) : zero16();
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    uint16_t* kl = lds + buf * S::kBufElems;
+    uint32_t* vl32 = reinterpret_cast<uint32_t*>(lds + buf * S::kBufElems + S::kKElems);
+#pragma unroll
+    for (int it = 0; it < S::kKIter; ++it) {
+      const int item = tid + 256 * it;
+      if (item < S::kKItems) {
+        const int row = item / S::kChunks;
+        const int ch = item - row * S::kChunks;
+        *reinterpret_cast<u32x4*>(kl + row * S::kKPitch + 8 * ch) = kreg[it];
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < S::kVIter; ++it) {
+      const int item = tid + 256 * it;
+      if (item < S::kVItems) {
+        const int pr = item / S::kChunks;
+        const int ch = item - pr * S::kChunks;
+        const int key = 2 * pr;                       // tile-local, even
+        const int pos = (key & ~15) + vt_pos16(key & 15);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int d = 8 * ch + t;
+          // 16-byte groups of a V^T row are XOR-swizzled by (d / 8) % 8 so
+          // that lanes writing the same row offset of different rows spread
+          // over the LDS banks.
+          const int grp = (pos >> 3) ^ ((d >> 3) & 7);
+          const int col = grp * 8 + (pos & 7);
+          const uint32_t lo = vreg[it][0][t >> 1], hi = vreg[it][1][t >> 1];
+          const uint32_t w = (t & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
+                                     : ((lo & 0xffffu) | (hi << 16));
+          vl32[(d * S::kVPitch + col) >> 1] = w;
+        }
+      }
+    }
+  };
+
+  f32x16 oacc[S::kND];
+#pragma unroll
+  for (int i = 0; i < S::kND; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
+  float m_run = kNegInf;  // running max of scaled scores, log2 domain
+  float l_run = 0.f;      // this lane's half of the running normaliser
+
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+
+  for (int t = 0; t < n_tiles; ++t) {
+    if (t + 1 < n_tiles) load_tile(t + 1);
+    __syncthreads();
+    const int kv0 = t * S::kBC;
+    const uint16_t* kl = lds + (t & 1) * S::kBufElems;
+    const uint16_t* vl = kl + S::kKElems;
+
+    const bool active = !CAUSAL || kv0 <= wave_last_row;
+    if (active) {
+      // ---- S^T = K Q^T for two 32-key blocks ----
+      f32x16 s[2];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
+        const uint16_t* krow = kl + (32 * sb + lq) * S::kKPitch + 8 * g;
+#pragma unroll
+        for (int kc = 0; kc < S::kKC; ++kc) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(krow + 16 * kc);
+          s[sb] = mfma32(a, qop[kc], s[sb]);
+        }
+      }
+
+      // ---- scale, mask, online softmax (log2 domain) ----
+      const bool need_mask = (kv0 + S::kBC > p.Lk) || (CAUSAL && kv0 + S::kBC - 1 > q0 + wave * 32);
+      float mx = kNegInf;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = s[sb][r] * p.scale_log2;
+          if (need_mask) {
+            const int key = kv0 + 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3);
+            const bool vis = key < p.Lk && (!CAUSAL || key <= qrow);
+            x = vis ? x : kNegInf;
+          }
+          s[sb][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = max_xor32(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+
+      float rs = 0.f;
+      u32x4 pop[4];  // P^T B operands, one per 16-key slice
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          float e[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            e[i] = fast_exp2(s[sb][8 * half + i] - m_new);
+            rs += e[i];
+          }
+          u32x4 pk;
+          pk[0] = pack_bf16x2(e[0], e[1]);
+          pk[1] = pack_bf16x2(e[2], e[3]);
+          pk[2] = pack_bf16x2(e[4], e[5]);
+          pk[3] = pack_bf16x2(e[6], e[7]);
+          pop[2 * sb + half] = pk;
+        }
+      l_run = l_run * alpha + rs;
+
+#pragma unroll
+      for (int db = 0; db < S::kND; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+
+      // ---- O^T += V^T P^T ----
+#pragma unroll
+      for (int db = 0; db < S::kND; ++db) {
+        const int d = 32 * db + lq;
+        const uint16_t* vrow = vl + d * S::kVPitch;
+        const int sw = (d >> 3) & 7;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int grp = (2 * c + g) ^ sw;
+          const u32x4 a = *reinterpret_cast<const u32x4*>(vrow + 8 * grp);
+          oacc[db] = mfma32(a, pop[c], oacc[db]);
+        }
+      }
+    }
+
+    if (t + 1 < n_tiles) store_tile((t + 1) & 1);
+  }
+
+  // ---- epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2 ----
+  const float l_tot = sum_xor32(l_run);
+  if (qrow < p.Lq) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)qrow * p.o_st;
+#pragma unroll
+    for (int db = 0; db < S::kND; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * db + 8 * j + 4 * g;
+        if (d < D) {
+          u32x2 w;
+          w[0] = pack_bf16x2(oacc[db][4 * j + 0] * inv, oacc[db][4 * j + 1] * inv);
+          w[1] = pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + d) = w;
+        }
+      }
+    if (g == 0) {
+      const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
+      p.lse[((int64_t)b * p.Hq + h) * p.Lq + qrow] = lse;
+    }
+  }
+}
+
+}  // namespace attn_dev

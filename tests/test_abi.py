@@ -1,0 +1,188 @@
+"""The C-ABI library on the host: it loads, exports what include/attn.h
+declares, and rejects every invalid argument before any device work.
+
+No GPU is needed: the validation functions make no HIP call, and attn_fwd /
+attn_decode return their error before touching the device.  The pointers used
+here are fake addresses that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import scaled_dot_product_qk_amd as sdpa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, NULL, SHAPE, DTYPE, LAYOUT, UNSUP, WS, HIP = range(8)
+P = 0x7f0000000000  # a 256-byte aligned fake device address
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = sdpa.lib()
+    declared = header_functions()
+    assert declared, "no declarations parsed"
+    assert set(declared) == set(sdpa.EXPORTED)
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sdpa.version().startswith("attn-gfx950")
+
+
+def test_status_strings():
+    for s in range(8):
+        assert sdpa.status_str(s) and sdpa.status_str(s) != "unknown status"
+    assert sdpa.status_str(99) == "unknown status"
+
+
+def fwd_args(**kw):
+    a = sdpa.FwdArgs()
+    B, Hq, Hkv, Lq, Lk, d = kw.get("B", 2), kw.get("Hq", 8), kw.get("Hkv", 2), kw.get("Lq", 300), \
+        kw.get("Lk", 300), kw.get("d", 64)
+    a.q, a.k, a.v, a.o, a.lse = [kw.get(n, P + i * 0x10000000) for i, n in
+                                 enumerate(("q", "k", "v", "o", "lse"))]
+    a.B, a.Hq, a.Hkv, a.Lq, a.Lk, a.d = B, Hq, Hkv, Lq, Lk, d
+    a.q_strides = sdpa._i64x3(*kw.get("qs", (Hq * Lq * d, Lq * d, d)))
+    a.k_strides = sdpa._i64x3(*kw.get("ks", (Hkv * Lk * d, Lk * d, d)))
+    a.v_strides = sdpa._i64x3(*kw.get("vs", (Hkv * Lk * d, Lk * d, d)))
+    a.o_strides = sdpa._i64x3(*kw.get("os", (Hq * Lq * d, Lq * d, d)))
+    a.dtype = kw.get("dtype", sdpa.ATTN_BF16)
+    a.causal = kw.get("causal", 0)
+    a.scale = kw.get("scale", 0.0)
+    return a
+
+
+def vfwd(**kw):
+    return sdpa.lib().attn_validate_fwd(ctypes.byref(fwd_args(**kw)))
+
+
+def run_fwd(**kw):
+    # Only reached with invalid arguments: attn_fwd returns before any HIP call.
+    return sdpa.lib().attn_fwd(ctypes.byref(fwd_args(**kw)), None)
+
+
+@pytest.mark.parametrize("d", [64, 80, 128])
+@pytest.mark.parametrize("dtype", [0, 1])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_fwd_valid_configurations(d, dtype, causal):
+    assert vfwd(d=d, dtype=dtype, causal=causal) == OK
+    name = sdpa.lib().attn_kernel_name(ctypes.byref(fwd_args(d=d, dtype=dtype, causal=causal))).decode()
+    assert name == f"attn_fwd_{'bf16' if dtype == 0 else 'f32'}_d{d}" + ("_causal" if causal else "")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), NULL), (dict(o=0), NULL), (dict(lse=0), NULL), (dict(k=0), NULL), (dict(v=0), NULL),
+    (dict(dtype=2), DTYPE), (dict(dtype=-1), DTYPE),
+    (dict(B=-1), SHAPE), (dict(Lq=-5), SHAPE), (dict(Hkv=0), SHAPE), (dict(Hq=8, Hkv=3), SHAPE),
+    (dict(causal=1, Lq=300, Lk=200), SHAPE), (dict(scale=float("nan")), SHAPE),
+    (dict(scale=float("inf")), SHAPE),
+    (dict(d=96), UNSUP), (dict(d=32), UNSUP), (dict(d=256), UNSUP), (dict(d=0), UNSUP),
+    (dict(q=P + 8), LAYOUT), (dict(k=P + 2), LAYOUT), (dict(lse=P + 4), LAYOUT),
+    (dict(qs=(8 * 300 * 64, 300 * 64, 68)), LAYOUT),   # token stride not a 16-byte multiple
+    (dict(ks=(-1, 300 * 64, 64)), LAYOUT),
+    (dict(dtype=1, qs=(8 * 300 * 64, 300 * 64, 66)), LAYOUT),
+    (dict(Lq=2 ** 31, Lk=2 ** 31), UNSUP),
+])
+def test_fwd_rejections(kw, status):
+    assert vfwd(**kw) == status
+    assert run_fwd(**kw) == status
+    assert sdpa.lib().attn_kernel_name(ctypes.byref(fwd_args(**kw))).decode() == "none"
+
+
+def test_fwd_empty_inputs_are_valid_noops():
+    assert vfwd(B=0) == OK and run_fwd(B=0) == OK
+    assert vfwd(Hq=0, Hkv=0) == OK and run_fwd(Hq=0, Hkv=0) == OK
+    assert vfwd(Lq=0) == OK and run_fwd(Lq=0) == OK
+    # no keys: valid (O = 0, LSE = -inf); k and v may be NULL then
+    assert vfwd(Lk=0, k=0, v=0) == OK
+    assert vfwd(Lk=0, causal=1) == SHAPE
+
+
+def test_fwd_null_struct():
+    L = sdpa.lib()
+    assert L.attn_validate_fwd(None) == NULL
+    assert L.attn_fwd(None, None) == NULL
+    assert L.attn_kernel_name(None).decode() == "none"
+
+
+def dec_args(**kw):
+    a = sdpa.DecodeArgs()
+    B, Hq, Hkv, Lmax, d = kw.get("B", 4), kw.get("Hq", 8), kw.get("Hkv", 2), kw.get("Lmax", 1000), \
+        kw.get("d", 128)
+    a.q, a.k_cache, a.v_cache, a.seqlens, a.o, a.lse = [
+        kw.get(n, P + i * 0x10000000) for i, n in
+        enumerate(("q", "k_cache", "v_cache", "seqlens", "o", "lse"))]
+    a.B, a.Hq, a.Hkv, a.Lmax, a.d = B, Hq, Hkv, Lmax, d
+    a.q_strides = sdpa._i64x2(*kw.get("qs", (Hq * d, d)))
+    a.k_strides = sdpa._i64x3(*kw.get("ks", (Hkv * Lmax * d, Lmax * d, d)))
+    a.v_strides = sdpa._i64x3(*kw.get("vs", (Hkv * Lmax * d, Lmax * d, d)))
+    a.o_strides = sdpa._i64x2(*kw.get("os", (Hq * d, d)))
+    a.dtype = kw.get("dtype", sdpa.ATTN_BF16)
+    a.scale = kw.get("scale", 0.0)
+    return a
+
+
+def vdec(**kw):
+    return sdpa.lib().attn_validate_decode(ctypes.byref(dec_args(**kw)))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (32, 8), (4, 4), (40, 1)])
+def test_decode_valid(d, Hq, Hkv):
+    assert vdec(d=d, Hq=Hq, Hkv=Hkv) == OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), NULL), (dict(seqlens=0), NULL), (dict(k_cache=0), NULL), (dict(lse=0), NULL),
+    (dict(dtype=7), DTYPE), (dict(dtype=1), UNSUP), (dict(d=80), UNSUP), (dict(d=96), UNSUP),
+    (dict(Hkv=3), SHAPE), (dict(Hkv=0), SHAPE), (dict(Lmax=-1), SHAPE),
+    (dict(scale=float("nan")), SHAPE),
+    (dict(q=P + 2), LAYOUT), (dict(seqlens=P + 2), LAYOUT), (dict(ks=(8 * 1000 * 128, 1000 * 128, 130)), LAYOUT),
+    (dict(B=70000), UNSUP),
+])
+def test_decode_rejections(kw, status):
+    assert vdec(**kw) == status
+    ws = sdpa.attn_decode_workspace_bytes(4, 8, 1000, 128)
+    assert sdpa.lib().attn_decode(ctypes.byref(dec_args(**kw)), P, ws, None) == status
+
+
+def test_decode_workspace_rules():
+    L = sdpa.lib()
+    need = sdpa.attn_decode_workspace_bytes(4, 8, 1000, 128)
+    # 2 chunks of 512 slots: O partials 4*8*2*128 floats (256-aligned) + LSE partials
+    assert need == 4 * 8 * 2 * 128 * 4 + 4 * 8 * 2 * 4
+    assert L.attn_decode(ctypes.byref(dec_args()), None, need, None) == WS
+    assert L.attn_decode(ctypes.byref(dec_args()), P, need - 1, None) == WS
+    assert L.attn_decode(ctypes.byref(dec_args()), P + 16, need, None) == LAYOUT
+    assert sdpa.attn_decode_workspace_bytes(-1, 8, 10, 128) == 0
+    assert sdpa.attn_decode_workspace_bytes(64, 32, 8192, 128) == 64 * 32 * 16 * 129 * 4
+    assert sdpa.attn_decode_workspace_bytes(2, 2, 0, 128) == 0
+
+
+def test_decode_empty_is_noop():
+    L = sdpa.lib()
+    assert vdec(B=0) == OK and L.attn_decode(ctypes.byref(dec_args(B=0)), None, 0, None) == OK
+    assert vdec(Hq=0, Hkv=0) == OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros(1, 2, 16, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sdpa.attn_fwd(q, q, q)
+    with pytest.raises(ValueError):
+        sdpa.attn_decode(torch.zeros(1, 2, 64, dtype=torch.bfloat16), q, q,
+                         torch.ones(1, dtype=torch.int32))
+
+
+def test_build_entry_point_exists():
+    import importlib
+    ge = importlib.import_module("__graft_entry__")
+    assert callable(ge.build) and callable(ge.smoke)
