@@ -1,0 +1,228 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of the whole path over synthetic, HBM-resident inputs:
+  1. attn_fwd, non-causal, B=1, H=96, n=4096, d=64, bf16     (headline workload)
+  2. attn_fwd, causal GQA, B=1, Hq=32, Hkv=8, n=8192, d=128, bf16
+  3. attn_decode, B=64, Hq=32, Hkv=8, d=128, cache lengths U{1024..8192}, bf16
+Each call is timed with HIP events recorded on the stream the kernels run on;
+the step as a whole is timed with host clocks between device synchronisations.
+
+Prints ONE JSON line.  `value` is the headline workload's attention-forward
+throughput in TFLOP/s (credited flops 4 n^2 d H B, halved when causal).
+`roofline` covers the headline kernel; the other two calls are reported in
+`extra` with their own rooflines (bf16 matrix peak for prefill, HBM peak for
+decode).  `cpu_baseline` times the CPU oracle on a bounded sample of the
+headline workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E peak
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "scaled_dot_product_qk_amd", "csrc", f)
+                  for f in ("attn_api.hip", "device_common.h", "fwd_bf16.h", "fwd_f32.h", "decode.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counted_traffic(tag: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary for
+    this kernel, or None if there is none or the kernel sources changed since
+    the counters were taken."""
+    path = os.path.join(PROFILES, f"{tag}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_val or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_val.group(1))
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["all", "fwd_n4096", "fwd_causal_n8192", "decode"], default="all",
+                    help="time one call of the step only (profiling runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-heads", type=int, default=96)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 256 * 2 ** 20  # bytes
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+
+
+def cpu_baseline(q, k, v, heads: int):
+    """The CPU oracle (untuned) on `heads` whole heads of the headline workload."""
+    from oracle import sdpa_oracle as orc
+    import workloads as wl
+    threads = min(os.cpu_count() or 1, heads, 16)  # at most 16 host threads
+    idx = list(range(heads))
+    t0 = time.perf_counter()
+    orc.attention_forward(q[:, idx], k[:, idx], v[:, idx], causal=False, threads=threads)
+    dt = time.perf_counter() - t0
+    B, _, L, d = q.shape
+    flops = wl.algorithmic_flops_fwd(B, heads, L, L, d, False)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} of 96 heads (all 4096 rows each) of the n=4096 d=64 workload, "
+                      f"float64 numpy, {dt:.2f} s wall"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU sharding is a "
+              "design note, not a measured path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import scaled_dot_product_qk_amd as sdpa
+    import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    names = ["fwd_n4096", "fwd_causal_n8192", "decode"] if args.only == "all" else [args.only]
+
+    # ---- inputs, generated on the host and copied once to HBM ----
+    calls = {}
+    if "fwd_n4096" in names:
+        q2, k2, v2 = wl.make_fwd_inputs(wl.C2)
+        G2 = [t.to(dev) for t in (q2, k2, v2)]
+        o2 = torch.empty_like(G2[0])
+        l2 = torch.empty(G2[0].shape[:3], dtype=torch.float32, device=dev)
+        calls["fwd_n4096"] = lambda: sdpa.attn_fwd(*G2, causal=False, out=o2, lse=l2, stream=stream)
+    if "fwd_causal_n8192" in names:
+        q4, k4, v4 = wl.make_fwd_inputs(wl.C4)
+        G4 = [t.to(dev) for t in (q4, k4, v4)]
+        del q4, k4, v4
+        o4 = torch.empty_like(G4[0])
+        l4 = torch.empty(G4[0].shape[:3], dtype=torch.float32, device=dev)
+        calls["fwd_causal_n8192"] = lambda: sdpa.attn_fwd(*G4, causal=True, out=o4, lse=l4, stream=stream)
+    if "decode" in names:
+        qd, kc, vc, lens = wl.make_decode_inputs(wl.C5)
+        GD = [t.to(dev) for t in (qd, kc, vc, lens)]
+        del kc, vc
+        od = torch.empty_like(GD[0])
+        ld = torch.empty(GD[0].shape[:2], dtype=torch.float32, device=dev)
+        ws = torch.empty(sdpa.attn_decode_workspace_bytes(wl.C5.B, wl.C5.Hq, wl.C5.Lmax, wl.C5.d),
+                         dtype=torch.uint8, device=dev)
+        calls["decode"] = lambda: sdpa.attn_decode(*GD, workspace=ws, out=od, lse=ld, stream=stream)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        for n in names:
+            calls[n]()
+    torch.cuda.synchronize()
+
+    ev = {n: [] for n in names}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for n in names:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            calls[n]()
+            b.record(stream)
+            ev[n].append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / len(ev[n]) for n in names}
+
+    # ---- accounting ----
+    C2, C4, C5 = wl.C2, wl.C4, wl.C5
+    f2 = wl.algorithmic_flops_fwd(C2.B, C2.Hq, C2.Lq, C2.Lk, C2.d, C2.causal)
+    f4 = wl.algorithmic_flops_fwd(C4.B, C4.Hq, C4.Lq, C4.Lk, C4.d, C4.causal)
+    res = {}
+    if "fwd_n4096" in ms:
+        t = ms["fwd_n4096"] / 1e3
+        res["fwd_n4096"] = {"kernel": sdpa.kernel_name(*G2, causal=False), "ms": ms["fwd_n4096"],
+                            "tflops": f2 / t / 1e12, "algorithmic_flops": f2}
+    if "fwd_causal_n8192" in ms:
+        t = ms["fwd_causal_n8192"] / 1e3
+        res["fwd_causal_n8192"] = {"kernel": sdpa.kernel_name(*G4, causal=True),
+                                   "ms": ms["fwd_causal_n8192"], "tflops": f4 / t / 1e12,
+                                   "algorithmic_flops": f4}
+    if "decode" in ms:
+        t = ms["decode"] / 1e3
+        bd = wl.algorithmic_bytes_decode(lens.tolist(), C5.Hq, C5.Hkv, C5.d, 2, C5.Lmax)
+        res["decode"] = {"kernel": "attn_decode_split_kernel<128> + attn_decode_merge_kernel<128>",
+                         "ms": ms["decode"], "gbps": bd / t / 1e9, "algorithmic_bytes": bd,
+                         "total_cache_keys": int(lens.sum())}
+
+    def roof_fwd(r, tag):
+        tr = counted_traffic(tag)
+        return {"bound": "mfma", "achieved": r["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": r["tflops"] / PEAK_BF16_TFLOPS, "traffic": tr}
+
+    headline = res.get("fwd_n4096")
+    out = {
+        "metric": "attention fwd TFLOPS (causal-adj) at n=4096-8192; decode HBM GB/s",
+        "value": headline["tflops"] if headline else None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded iid N(0,1), bf16 round-to-nearest-even)",
+        "config": {"workload": "fwd_bf16_b1_h96_n4096_d64 (non-causal)",
+                   "step": names, "B": 1, "H": 96, "n": 4096, "d": 64},
+        "roofline": roof_fwd(headline, "attn_fwd_bf16_d64_n4096") if headline else None,
+        "extra": {},
+    }
+    if "fwd_causal_n8192" in res:
+        r = res["fwd_causal_n8192"]
+        out["extra"]["fwd_causal_gqa_n8192_d128"] = dict(r, roofline=roof_fwd(r, "attn_fwd_bf16_d128_causal_n8192"))
+    if "decode" in res:
+        r = res["decode"]
+        out["extra"]["decode_b64_gqa_d128"] = dict(r, roofline={
+            "bound": "hbm", "achieved": r["gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": r["gbps"] / PEAK_HBM_GBPS, "traffic": counted_traffic("attn_decode_d128_b64")})
+    if headline:
+        out["extra"]["fwd_n4096_d64"] = headline
+    if not args.no_cpu_baseline and args.only in ("all", "fwd_n4096"):
+        out["cpu_baseline"] = cpu_baseline(q2, k2, v2, args.cpu_sample_heads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
