@@ -33,6 +33,7 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     tmp = out + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function",
            *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
     if extra_flags:

@@ -65,7 +65,8 @@ extern "C" attn_status_t attn_validate_fwd(const attn_fwd_args_t* a) {
     return ATTN_ERR_LAYOUT;
   // Index ranges the kernels keep in 32 bits, and the grid limits.
   if (a->Lq > kI32Max || a->Lk > kI32Max || a->B * a->Hq > kI32Max) return ATTN_ERR_UNSUPPORTED;
-  if ((a->Lq + 127) / 128 > kGridYMax) return ATTN_ERR_UNSUPPORTED;
+  if ((a->Lq + 127) / 128 > kGridYMax || a->B * a->Hq * ((a->Lq + 127) / 128) > kI32Max)
+    return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 
@@ -99,7 +100,7 @@ static attn_status_t launch_fwd_bf16(const FwdParams& p, int grid_x, hipStream_t
       return ATTN_ERR_HIP;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(grid_x, p.n_qtiles), dim3(256), lds, s, p);
+  hipLaunchKernelGGL(kern, dim3(grid_x * p.n_qtiles), dim3(256), lds, s, p);
   return launch_status();
 }
 
@@ -131,11 +132,14 @@ extern "C" attn_status_t attn_fwd(const attn_fwd_args_t* a, void* stream) {
   p.v_sb = a->v_strides[0]; p.v_sh = a->v_strides[1]; p.v_st = a->v_strides[2];
   p.o_sb = a->o_strides[0]; p.o_sh = a->o_strides[1]; p.o_st = a->o_strides[2];
   p.Hq = (int)a->Hq;
+  p.Hkv = (int)a->Hkv;
   p.group = (int)(a->Hq / a->Hkv);
   p.Lq = (int)a->Lq;
   p.Lk = (int)a->Lk;
   p.n_qtiles = (int)((a->Lq + 127) / 128);
   p.scale_log2 = effective_scale(a->scale, a->d) * kLog2e;
+  p.scale_log2_abs = std::fabs(p.scale_log2);
+  p.neg_q = p.scale_log2 < 0.f ? 1 : 0;
   const int grid_x = (int)(a->B * a->Hq);
   const bool c = a->causal != 0;
 

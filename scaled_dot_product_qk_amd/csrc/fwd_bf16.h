@@ -30,6 +30,8 @@
 // on and exp(-inf - m) = 0 never meets exp(-inf - (-inf)).
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace attn_dev {
@@ -45,12 +47,43 @@ struct FwdParams {
   int64_t v_sb, v_sh, v_st;
   int64_t o_sb, o_sh, o_st;
   int Hq;
+  int Hkv;
   int group;  // Hq / Hkv
   int Lq;
   int Lk;
   int n_qtiles;
-  float scale_log2;  // scale * log2(e)
+  float scale_log2;      // scale * log2(e)
+  float scale_log2_abs;  // |scale * log2(e)|
+  int neg_q;             // scale < 0: Q's sign bits are flipped on load (exact)
 };
+
+// Work-item order shared by the prefill kernels.  The hardware hands
+// consecutive workgroup ids to the 8 XCDs in turn; this maps them so that each
+// XCD receives one contiguous range of work items, and orders work items kv
+// head by kv head, so the workgroups that re-read one head's K and V run on
+// the same XCD and share its L2.  Within a kv head: query tiles (heaviest
+// first when causal), then the query heads of the group.
+struct WorkItem {
+  int b, h, hk, qt;
+};
+
+__device__ __forceinline__ WorkItem prefill_work_item(const FwdParams& p, bool causal) {
+  const int L = blockIdx.x;
+  const int N = gridDim.x;
+  const int full = N & ~7;
+  int w = L;
+  if (L < full) w = (L & 7) * (full >> 3) + (L >> 3);
+  WorkItem it;
+  const int hg = w % p.group;
+  int r = w / p.group;
+  const int qi = r % p.n_qtiles;
+  r /= p.n_qtiles;
+  it.hk = r % p.Hkv;
+  it.b = r / p.Hkv;
+  it.h = it.hk * p.group + hg;
+  it.qt = causal ? p.n_qtiles - 1 - qi : qi;
+  return it;
+}
 
 template <int D>
 struct Bf16FwdShape {
@@ -81,6 +114,14 @@ __device__ __forceinline__ int vt_pos16(int kk) {
   return ((kk >> 2) & 1) * 8 + (kk >> 3) * 4 + (kk & 3);
 }
 
+// Row maxima are tracked in the log2 domain of the scaled scores.  The output
+// and the normaliser are rescaled only when some row's tile maximum exceeds
+// the reference maximum by more than this many binary orders (a wave-uniform
+// decision); otherwise the probabilities are formed against the stale
+// reference and stay below 2^kRescaleLog2, well inside fp32 and bf16 range.
+// LSE = ref + log2(l) is exact either way.
+constexpr float kRescaleLog2 = 8.0f;
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdParams p) {
   using S = Bf16FwdShape<D>;
@@ -92,12 +133,9 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdParams p) {
   const int lq = lane & 31;  // query row within the wave (n index)
   const int g = lane >> 5;   // lane half
 
-  const int bh = blockIdx.x;
-  const int b = bh / p.Hq;
-  const int h = bh - b * p.Hq;
-  const int hk = h / p.group;
-  const int qt = CAUSAL ? (p.n_qtiles - 1 - (int)blockIdx.y) : (int)blockIdx.y;
-  const int q0 = qt * S::kBR;
+  const WorkItem wi = prefill_work_item(p, CAUSAL);
+  const int b = wi.b, h = wi.h, hk = wi.hk;
+  const int q0 = wi.qt * S::kBR;
   const int qrow = q0 + wave * 32 + lq;
 
   const uint16_t* qg = reinterpret_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh;
@@ -109,9 +147,15 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdParams p) {
   {
     const bool ok = qrow < p.Lq;
     const uint16_t* qr = qg + (int64_t)qrow * p.q_st + 8 * g;
+    const uint32_t flip = p.neg_q ? 0x80008000u : 0u;
 #pragma unroll
-    for (int kc = 0; kc < S::kKC; ++kc) qop[kc] = ok ? load16(qr + 16 * kc) : zero16();
+    for (int kc = 0; kc < S::kKC; ++kc) {
+      qop[kc] = ok ? load16(qr + 16 * kc) : zero16();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qop[kc][e] ^= flip;
+    }
   }
+  const float c = p.scale_log2_abs;
 
   // Key tiles this workgroup visits.
   int kv_end = p.Lk;
@@ -129,28 +173,35 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdParams p) {
   }
 
   // ---- global -> register staging of one key tile ----
-  u32x4 kreg[S::kKIter];
-  u32x4 vreg[S::kVIter][2];
+  u32x4 kreg[S::kKIter] = {};
+  u32x4 vreg[S::kVIter][2] = {};
 
+  // Rows at or beyond Lk are read from row Lk - 1 instead (always in bounds,
+  // always finite); their scores are masked to -inf, so they carry weight 0.
+  const int last_key = p.Lk - 1;
   auto load_tile = [&](int t) {
     const int kv0 = t * S::kBC;
 #pragma unroll
     for (int it = 0; it < S::kKIter; ++it) {
       const int item = tid + 256 * it;
-      const int row = item / S::kChunks;
-      const int ch = item - row * S::kChunks;
-      const bool ok = (item < S::kKItems) && (kv0 + row < p.Lk);
-      kreg[it] = ok ? load16(kg + (int64_t)(kv0 + row) * p.k_st + 8 * ch) : zero16();
+      if (S::kKItems % 256 == 0 || item < S::kKItems) {
+        const int row = item / S::kChunks;
+        const int ch = item - row * S::kChunks;
+        const int key = min(kv0 + row, last_key);
+        kreg[it] = load16(kg + (int64_t)key * p.k_st + 8 * ch);
+      }
     }
 #pragma unroll
     for (int it = 0; it < S::kVIter; ++it) {
       const int item = tid + 256 * it;
-      const int pr = item / S::kChunks;  // key pair
-      const int ch = item - pr * S::kChunks;
-      const bool in = item < S::kVItems;
-      const int key = kv0 + 2 * pr;
-      vreg[it][0] = (in && key < p.Lk) ? load16(vg + (int64_t)key * p.v_st + 8 * ch) : zero16();
-      vreg[it][1] = (in && key + 1 < p.Lk) ? load16(vg + (int64_t)(key + 1) * p.v_st + 8 * ch) : zero16();
+      if (S::kVItems % 256 == 0 || item < S::kVItems) {
+        const int pr = item / S::kChunks;  // key pair
+        const int ch = item - pr * S::kChunks;
+        const int key0 = min(kv0 + 2 * pr, last_key);
+        const int key1 = min(kv0 + 2 * pr + 1, last_key);
+        vreg[it][0] = load16(vg + (int64_t)key0 * p.v_st + 8 * ch);
+        vreg[it][1] = load16(vg + (int64_t)key1 * p.v_st + 8 * ch);
+      }
     }
   };
 
@@ -182,9 +233,9 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdParams p) {
           // over the LDS banks.
           const int grp = (pos >> 3) ^ ((d >> 3) & 7);
           const int col = grp * 8 + (pos & 7);
-          const uint32_t lo = vreg[it][0][t >> 1], hi = vreg[it][1][t >> 1];
-          const uint32_t w = (t & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
-                                     : ((lo & 0xffffu) | (hi << 16));
+          // (key, key + 1) pair of element t: low or high halves of the two rows.
+          const uint32_t w = __builtin_amdgcn_perm(vreg[it][1][t >> 1], vreg[it][0][t >> 1],
+                                                   (t & 1) ? 0x07060302u : 0x05040100u);
           vl32[(d * S::kVPitch + col) >> 1] = w;
         }
       }
@@ -196,99 +247,115 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdParams p) {
   for (int i = 0; i < S::kND; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
-  float m_run = kNegInf;  // running max of scaled scores, log2 domain
-  float l_run = 0.f;      // this lane's half of the running normaliser
+  float m_run = kNegInf;  // reference max of scaled scores, log2 domain
+  float l_run = 0.f;      // this lane's half of the normaliser
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-
-  for (int t = 0; t < n_tiles; ++t) {
-    if (t + 1 < n_tiles) load_tile(t + 1);
-    __syncthreads();
-    const int kv0 = t * S::kBC;
-    const uint16_t* kl = lds + (t & 1) * S::kBufElems;
-    const uint16_t* vl = kl + S::kKElems;
-
-    const bool active = !CAUSAL || kv0 <= wave_last_row;
-    if (active) {
-      // ---- S^T = K Q^T for two 32-key blocks ----
-      f32x16 s[2];
+  // One key tile: S^T, online softmax, O^T += V^T P^T.  MASK selects the
+  // variant that masks keys beyond Lk and (causal) keys after the query.
+  auto process = [&](auto mask_tag, const uint16_t* kl, const uint16_t* vl, int kv0) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    f32x16 s[2];
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
+    for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
-        const uint16_t* krow = kl + (32 * sb + lq) * S::kKPitch + 8 * g;
+      for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
+      const uint16_t* krow = kl + (32 * sb + lq) * S::kKPitch + 8 * g;
 #pragma unroll
-        for (int kc = 0; kc < S::kKC; ++kc) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(krow + 16 * kc);
-          s[sb] = mfma32(a, qop[kc], s[sb]);
-        }
+      for (int kc = 0; kc < S::kKC; ++kc) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + 16 * kc);
+        s[sb] = mfma32(a, qop[kc], s[sb]);
       }
+    }
 
-      // ---- scale, mask, online softmax (log2 domain) ----
-      const bool need_mask = (kv0 + S::kBC > p.Lk) || (CAUSAL && kv0 + S::kBC - 1 > q0 + wave * 32);
-      float mx = kNegInf;
+    // Tile max on the raw scores (the scale is positive).
+    float mx = kNegInf;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[sb][r] * p.scale_log2;
-          if (need_mask) {
-            const int key = kv0 + 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3);
-            const bool vis = key < p.Lk && (!CAUSAL || key <= qrow);
-            x = vis ? x : kNegInf;
-          }
-          s[sb][r] = x;
-          mx = fmaxf(mx, x);
+      for (int r = 0; r < 16; ++r) {
+        if constexpr (MASK) {
+          const int key = kv0 + 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool vis = key < p.Lk && (!CAUSAL || key <= qrow);
+          s[sb][r] = vis ? s[sb][r] : kNegInf;
         }
-      mx = max_xor32(mx);
-      const float m_new = fmaxf(m_run, mx);
+        mx = fmaxf(mx, s[sb][r]);
+      }
+    const float mt = max_xor32(mx) * c;
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2) != 0) {
+      const float m_new = fmaxf(m_run, mt);
       const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
-
-      float rs = 0.f;
-      u32x4 pop[4];  // P^T B operands, one per 16-key slice
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          float e[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            e[i] = fast_exp2(s[sb][8 * half + i] - m_new);
-            rs += e[i];
-          }
-          u32x4 pk;
-          pk[0] = pack_bf16x2(e[0], e[1]);
-          pk[1] = pack_bf16x2(e[2], e[3]);
-          pk[2] = pack_bf16x2(e[4], e[5]);
-          pk[3] = pack_bf16x2(e[6], e[7]);
-          pop[2 * sb + half] = pk;
-        }
-      l_run = l_run * alpha + rs;
-
+      l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < S::kND; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    const float neg_m = -m_run;
 
-      // ---- O^T += V^T P^T ----
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short dependency chains
+    u32x4 pop[4];  // P^T B operands, one per 16-key slice
 #pragma unroll
-      for (int db = 0; db < S::kND; ++db) {
-        const int d = 32 * db + lq;
-        const uint16_t* vrow = vl + d * S::kVPitch;
-        const int sw = (d >> 3) & 7;
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int grp = (2 * c + g) ^ sw;
-          const u32x4 a = *reinterpret_cast<const u32x4*>(vrow + 8 * grp);
-          oacc[db] = mfma32(a, pop[c], oacc[db]);
+      for (int half = 0; half < 2; ++half) {
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          e[i] = fast_exp2(__builtin_fmaf(s[sb][8 * half + i], c, neg_m));
+          rs[i & 3] += e[i];
         }
+        u32x4 pk;
+        pk[0] = pack_bf16x2(e[0], e[1]);
+        pk[1] = pack_bf16x2(e[2], e[3]);
+        pk[2] = pack_bf16x2(e[4], e[5]);
+        pk[3] = pack_bf16x2(e[6], e[7]);
+        pop[2 * sb + half] = pk;
+      }
+    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+
+#pragma unroll
+    for (int db = 0; db < S::kND; ++db) {
+      const int d = 32 * db + lq;
+      const uint16_t* vrow = vl + d * S::kVPitch;
+      const int sw = (d >> 3) & 7;
+#pragma unroll
+      for (int cs = 0; cs < 4; ++cs) {
+        const int grp = (2 * cs + g) ^ sw;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(vrow + 8 * grp);
+        oacc[db] = mfma32(a, pop[cs], oacc[db]);
       }
     }
+  };
 
+  if (n_tiles > 0) {
+    // Q must have landed before the loop: the compiler's in-order view of
+    // outstanding loads would otherwise make the first use of Q inside the
+    // loop wait for the next tile's prefetch as well.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    load_tile(0);
+    store_tile(0);
+  }
+
+  // Tiles that need no mask for any wave of the workgroup come first (one
+  // code path per loop keeps the accumulators in place); the tail of the key
+  // range and the diagonal tiles follow with the masked path.
+  int n_plain = min(n_tiles, p.Lk / S::kBC);
+  if (CAUSAL) n_plain = min(n_plain, (q0 + 1) / S::kBC);
+  int t = 0;
+  for (; t < n_plain; ++t) {
+    if (t + 1 < n_tiles) load_tile(t + 1);
+    __syncthreads();
+    const uint16_t* kl = lds + (t & 1) * S::kBufElems;
+    process(std::false_type{}, kl, kl + S::kKElems, t * S::kBC);
+    if (t + 1 < n_tiles) store_tile((t + 1) & 1);
+  }
+  for (; t < n_tiles; ++t) {
+    if (t + 1 < n_tiles) load_tile(t + 1);
+    __syncthreads();
+    const int kv0 = t * S::kBC;
+    const uint16_t* kl = lds + (t & 1) * S::kBufElems;
+    if (!CAUSAL || kv0 <= wave_last_row) process(std::true_type{}, kl, kl + S::kKElems, kv0);
     if (t + 1 < n_tiles) store_tile((t + 1) & 1);
   }
 
