@@ -100,7 +100,9 @@ static attn_status_t launch_fwd_bf16(const FwdParams& p, int grid_x, hipStream_t
       return ATTN_ERR_HIP;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(grid_x * p.n_qtiles), dim3(256), lds, s, p);
+  FwdParams q = p;
+  q.n_qtiles = (p.Lq + Bf16FwdShape<D>::kBR - 1) / Bf16FwdShape<D>::kBR;
+  hipLaunchKernelGGL(kern, dim3(grid_x * q.n_qtiles), dim3(256), lds, s, q);
   return launch_status();
 }
 

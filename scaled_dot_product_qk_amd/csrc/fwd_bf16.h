@@ -85,26 +85,37 @@ __device__ __forceinline__ WorkItem prefill_work_item(const FwdParams& p, bool c
   return it;
 }
 
+// 32-query column blocks per wave: two at head_dim 64 (each K or V^T read
+// from LDS then feeds two matrix instructions), one at larger head_dims where
+// the output accumulator alone would not leave room for two waves per SIMD.
+__host__ __device__ constexpr int bf16_fwd_blocks_per_wave(int d) { return d <= 64 ? 2 : 1; }
+__host__ __device__ constexpr int bf16_fwd_rows_per_workgroup(int d) {
+  return 4 * 32 * bf16_fwd_blocks_per_wave(d);
+}
+
 template <int D>
 struct Bf16FwdShape {
   static constexpr int kWaves = 4;
-  static constexpr int kBR = 32 * kWaves;        // query rows per workgroup
-  static constexpr int kBC = 64;                 // keys per tile
-  static constexpr int kKC = D / 16;             // k-slices of the Q K^T product
-  static constexpr int kDP = (D + 31) / 32 * 32; // rows of O^T padded to 32
-  static constexpr int kND = kDP / 32;           // 32-row blocks of O^T
-  static constexpr int kChunks = D / 8;          // 16-byte chunks per row
-  static constexpr int kKPitch = D + 8;          // K row pitch in LDS (elements)
-  static constexpr int kVPitch = kBC + 8;        // V^T row pitch in LDS (elements)
+  static constexpr int kNB = bf16_fwd_blocks_per_wave(D);
+  static constexpr int kRowsPerWave = 32 * kNB;
+  static constexpr int kBR = kRowsPerWave * kWaves;  // query rows per workgroup
+  static constexpr int kBC = 64;                     // keys per tile
+  static constexpr int kKC = D / 16;                 // k-slices of the Q K^T product
+  static constexpr int kDP = (D + 31) / 32 * 32;     // rows of O^T padded to 32
+  static constexpr int kND = kDP / 32;               // 32-row blocks of O^T
+  static constexpr int kChunks = D / 8;              // 16-byte chunks per row
+  static constexpr int kKPitch = D + 8;              // K row pitch in LDS (elements)
+  static constexpr int kVPitch = kBC + 8;            // V^T row pitch in LDS (elements)
   static constexpr int kKElems = kBC * kKPitch;
   static constexpr int kVElems = kDP * kVPitch;
-  static constexpr int kBufElems = kKElems + kVElems;
-  static constexpr int kLdsBytes = 2 * kBufElems * 2;
+  static constexpr int kBufBytes = (kKElems + kVElems) * 2;
+  static constexpr int kLdsBytes = 2 * kBufBytes;
   static constexpr int kKItems = kBC * kChunks;         // 16-byte K loads per tile
   static constexpr int kVItems = (kBC / 2) * kChunks;   // (key pair, chunk) V loads
   static constexpr int kKIter = (kKItems + 255) / 256;
   static constexpr int kVIter = (kVItems + 255) / 256;
   static_assert(D % 16 == 0, "head_dim must be a multiple of 16");
+  static_assert(kBufBytes < 65536, "in-buffer LDS offsets must fit the instruction offset field");
 };
 
 // Position of key kk (0..15) of a 16-key slice inside V^T's LDS row: the
@@ -123,36 +134,44 @@ __device__ __forceinline__ int vt_pos16(int kk) {
 constexpr float kRescaleLog2 = 8.0f;
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdParams p) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams p) {
   using S = Bf16FwdShape<D>;
+  constexpr int NB = S::kNB;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  char* const lds_b = reinterpret_cast<char*>(lds);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int lq = lane & 31;  // query row within the wave (n index)
+  const int lq = lane & 31;  // query column within a 32-query block (n index)
   const int g = lane >> 5;   // lane half
 
   const WorkItem wi = prefill_work_item(p, CAUSAL);
   const int b = wi.b, h = wi.h, hk = wi.hk;
   const int q0 = wi.qt * S::kBR;
-  const int qrow = q0 + wave * 32 + lq;
+  const int row0 = q0 + wave * S::kRowsPerWave;  // first query row of this wave
+  int qrow[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) qrow[nb] = row0 + 32 * nb + lq;
 
   const uint16_t* qg = reinterpret_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh;
   const uint16_t* kg = reinterpret_cast<const uint16_t*>(p.k) + b * p.k_sb + hk * p.k_sh;
   const uint16_t* vg = reinterpret_cast<const uint16_t*>(p.v) + b * p.v_sb + hk * p.v_sh;
 
   // Q^T as the B operand of S^T = K Q^T: lane holds Q[qrow][16*kc + 8*g .. +8].
-  u32x4 qop[S::kKC];
+  u32x4 qop[NB][S::kKC];
   {
-    const bool ok = qrow < p.Lq;
-    const uint16_t* qr = qg + (int64_t)qrow * p.q_st + 8 * g;
     const uint32_t flip = p.neg_q ? 0x80008000u : 0u;
 #pragma unroll
-    for (int kc = 0; kc < S::kKC; ++kc) {
-      qop[kc] = ok ? load16(qr + 16 * kc) : zero16();
+    for (int nb = 0; nb < NB; ++nb) {
+      const bool ok = qrow[nb] < p.Lq;
+      const uint16_t* qr = qg + (int64_t)qrow[nb] * p.q_st + 8 * g;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qop[kc][e] ^= flip;
+      for (int kc = 0; kc < S::kKC; ++kc) {
+        qop[nb][kc] = ok ? load16(qr + 16 * kc) : zero16();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qop[nb][kc][e] ^= flip;
+      }
     }
   }
   const float c = p.scale_log2_abs;
@@ -161,171 +180,212 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdParams p) {
   int kv_end = p.Lk;
   if (CAUSAL) kv_end = min(kv_end, q0 + S::kBR);
   const int n_tiles = (kv_end + S::kBC - 1) / S::kBC;
-  const int wave_last_row = q0 + wave * 32 + 31;
+  const int n_full = p.Lk / S::kBC;  // tiles with no key beyond Lk
+  const int wave_last_row = row0 + S::kRowsPerWave - 1;
 
   // Zero the padded rows of V^T (head_dim not a multiple of 32) once; the
   // loader never writes them and their products land in discarded O^T rows.
   if (S::kDP != D) {
     for (int i = tid; i < (S::kDP - D) * S::kVPitch; i += 256) {
       lds[S::kKElems + D * S::kVPitch + i] = 0;
-      lds[S::kBufElems + S::kKElems + D * S::kVPitch + i] = 0;
+      lds[S::kBufBytes / 2 + S::kKElems + D * S::kVPitch + i] = 0;
     }
   }
 
-  // ---- global -> register staging of one key tile ----
+  // ---- per-thread loader plan ----
+  // K: item -> (key row, 16-byte chunk), chunk fastest (coalesced rows).
+  // V: item -> (key pair, chunk), key pair fastest, so that the 4-byte V^T
+  //    writes of one instruction hit 32 different LDS banks.
+  int64_t koff[S::kKIter];
+  int kst[S::kKIter];
+  int64_t voff[S::kVIter];
+  int vst[S::kVIter];
+#pragma unroll
+  for (int it = 0; it < S::kKIter; ++it) {
+    const int item = tid + 256 * it;
+    const int row = item / S::kChunks, ch = item - (item / S::kChunks) * S::kChunks;
+    koff[it] = (int64_t)row * p.k_st + 8 * ch;
+    kst[it] = (row * S::kKPitch + 8 * ch) * 2;
+  }
+#pragma unroll
+  for (int it = 0; it < S::kVIter; ++it) {
+    const int item = tid + 256 * it;
+    const int pr = item & 31, ch = item >> 5;
+    const int key = 2 * pr;
+    voff[it] = (int64_t)key * p.v_st + 8 * ch;
+    vst[it] = S::kKElems * 2 + (8 * ch * S::kVPitch + (key & ~15) + vt_pos16(key & 15)) * 2;
+  }
+
   u32x4 kreg[S::kKIter] = {};
   u32x4 vreg[S::kVIter][2] = {};
 
-  // Rows at or beyond Lk are read from row Lk - 1 instead (always in bounds,
-  // always finite); their scores are masked to -inf, so they carry weight 0.
-  const int last_key = p.Lk - 1;
+  // Full tiles load without checks; the tile holding key Lk - 1 reads rows
+  // beyond it from row Lk - 1 instead (in bounds and finite), and those keys
+  // are masked to -inf, so they carry weight 0.
   auto load_tile = [&](int t) {
     const int kv0 = t * S::kBC;
+    if (t < n_full) {
+      const uint16_t* kt = kg + (int64_t)kv0 * p.k_st;
+      const uint16_t* vt = vg + (int64_t)kv0 * p.v_st;
 #pragma unroll
-    for (int it = 0; it < S::kKIter; ++it) {
-      const int item = tid + 256 * it;
-      if (S::kKItems % 256 == 0 || item < S::kKItems) {
-        const int row = item / S::kChunks;
-        const int ch = item - row * S::kChunks;
-        const int key = min(kv0 + row, last_key);
-        kreg[it] = load16(kg + (int64_t)key * p.k_st + 8 * ch);
+      for (int it = 0; it < S::kKIter; ++it)
+        if (S::kKItems % 256 == 0 || tid + 256 * it < S::kKItems) kreg[it] = load16(kt + koff[it]);
+#pragma unroll
+      for (int it = 0; it < S::kVIter; ++it)
+        if (S::kVItems % 256 == 0 || tid + 256 * it < S::kVItems) {
+          vreg[it][0] = load16(vt + voff[it]);
+          vreg[it][1] = load16(vt + voff[it] + p.v_st);
+        }
+    } else {
+      const int last = p.Lk - 1;
+#pragma unroll
+      for (int it = 0; it < S::kKIter; ++it) {
+        const int item = tid + 256 * it;
+        if (S::kKItems % 256 == 0 || item < S::kKItems) {
+          const int row = item / S::kChunks, ch = item - (item / S::kChunks) * S::kChunks;
+          kreg[it] = load16(kg + (int64_t)min(kv0 + row, last) * p.k_st + 8 * ch);
+        }
       }
-    }
 #pragma unroll
-    for (int it = 0; it < S::kVIter; ++it) {
-      const int item = tid + 256 * it;
-      if (S::kVItems % 256 == 0 || item < S::kVItems) {
-        const int pr = item / S::kChunks;  // key pair
-        const int ch = item - pr * S::kChunks;
-        const int key0 = min(kv0 + 2 * pr, last_key);
-        const int key1 = min(kv0 + 2 * pr + 1, last_key);
-        vreg[it][0] = load16(vg + (int64_t)key0 * p.v_st + 8 * ch);
-        vreg[it][1] = load16(vg + (int64_t)key1 * p.v_st + 8 * ch);
+      for (int it = 0; it < S::kVIter; ++it) {
+        const int item = tid + 256 * it;
+        if (S::kVItems % 256 == 0 || item < S::kVItems) {
+          const int pr = item & 31, ch = item >> 5;
+          vreg[it][0] = load16(vg + (int64_t)min(kv0 + 2 * pr, last) * p.v_st + 8 * ch);
+          vreg[it][1] = load16(vg + (int64_t)min(kv0 + 2 * pr + 1, last) * p.v_st + 8 * ch);
+        }
       }
     }
   };
 
   auto store_tile = [&](int buf) {
-    uint16_t* kl = lds + buf * S::kBufElems;
-    uint32_t* vl32 = reinterpret_cast<uint32_t*>(lds + buf * S::kBufElems + S::kKElems);
+    char* base = lds_b + buf * S::kBufBytes;
 #pragma unroll
-    for (int it = 0; it < S::kKIter; ++it) {
-      const int item = tid + 256 * it;
-      if (item < S::kKItems) {
-        const int row = item / S::kChunks;
-        const int ch = item - row * S::kChunks;
-        *reinterpret_cast<u32x4*>(kl + row * S::kKPitch + 8 * ch) = kreg[it];
-      }
-    }
+    for (int it = 0; it < S::kKIter; ++it)
+      if (S::kKItems % 256 == 0 || tid + 256 * it < S::kKItems)
+        *reinterpret_cast<u32x4*>(base + kst[it]) = kreg[it];
 #pragma unroll
-    for (int it = 0; it < S::kVIter; ++it) {
-      const int item = tid + 256 * it;
-      if (item < S::kVItems) {
-        const int pr = item / S::kChunks;
-        const int ch = item - pr * S::kChunks;
-        const int key = 2 * pr;                       // tile-local, even
-        const int pos = (key & ~15) + vt_pos16(key & 15);
+    for (int it = 0; it < S::kVIter; ++it)
+      if (S::kVItems % 256 == 0 || tid + 256 * it < S::kVItems) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const int d = 8 * ch + t;
-          // 16-byte groups of a V^T row are XOR-swizzled by (d / 8) % 8 so
-          // that lanes writing the same row offset of different rows spread
-          // over the LDS banks.
-          const int grp = (pos >> 3) ^ ((d >> 3) & 7);
-          const int col = grp * 8 + (pos & 7);
-          // (key, key + 1) pair of element t: low or high halves of the two rows.
+          // (key, key + 1) pair of head_dim element 8*ch + t: low or high
+          // halves of the two rows' words.
           const uint32_t w = __builtin_amdgcn_perm(vreg[it][1][t >> 1], vreg[it][0][t >> 1],
                                                    (t & 1) ? 0x07060302u : 0x05040100u);
-          vl32[(d * S::kVPitch + col) >> 1] = w;
+          *reinterpret_cast<uint32_t*>(base + vst[it] + t * S::kVPitch * 2) = w;
         }
       }
-    }
   };
 
-  f32x16 oacc[S::kND];
+  // Per-lane LDS read bases: K rows lq (+32 per key block), V^T rows lq (+32
+  // per head_dim block); every other offset is a compile-time constant.
+  const int k_rd = (lq * S::kKPitch + 8 * g) * 2;
+  const int v_rd = S::kKElems * 2 + (lq * S::kVPitch + 8 * g) * 2;
+
+  f32x16 oacc[NB][S::kND];
 #pragma unroll
-  for (int i = 0; i < S::kND; ++i)
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
-  float m_run = kNegInf;  // reference max of scaled scores, log2 domain
-  float l_run = 0.f;      // this lane's half of the normaliser
+    for (int i = 0; i < S::kND; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[nb][i][r] = 0.f;
+  float m_run[NB], l_run[NB];  // reference max (log2 domain), this lane's half of l
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    m_run[nb] = kNegInf;
+    l_run[nb] = 0.f;
+  }
 
   // One key tile: S^T, online softmax, O^T += V^T P^T.  MASK selects the
   // variant that masks keys beyond Lk and (causal) keys after the query.
-  auto process = [&](auto mask_tag, const uint16_t* kl, const uint16_t* vl, int kv0) {
+  auto process = [&](auto mask_tag, int buf, int kv0) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    f32x16 s[2];
+    const char* kb = lds_b + buf * S::kBufBytes + k_rd;
+    const char* vb = lds_b + buf * S::kBufBytes + v_rd;
+    f32x16 s[NB][2];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
-      const uint16_t* krow = kl + (32 * sb + lq) * S::kKPitch + 8 * g;
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[nb][sb][r] = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int kc = 0; kc < S::kKC; ++kc) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + 16 * kc);
-        s[sb] = mfma32(a, qop[kc], s[sb]);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kb + (32 * sb * S::kKPitch + 16 * kc) * 2);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) s[nb][sb] = mfma32(a, qop[nb][kc], s[nb][sb]);
       }
-    }
 
     // Tile max on the raw scores (the scale is positive).
-    float mx = kNegInf;
+    float mt[NB];
+    bool grow = false;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+    for (int nb = 0; nb < NB; ++nb) {
+      float mx = kNegInf;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if constexpr (MASK) {
-          const int key = kv0 + 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool vis = key < p.Lk && (!CAUSAL || key <= qrow);
-          s[sb][r] = vis ? s[sb][r] : kNegInf;
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if constexpr (MASK) {
+            const int key = kv0 + 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3);
+            const bool vis = key < p.Lk && (!CAUSAL || key <= qrow[nb]);
+            s[nb][sb][r] = vis ? s[nb][sb][r] : kNegInf;
+          }
+          mx = fmaxf(mx, s[nb][sb][r]);
         }
-        mx = fmaxf(mx, s[sb][r]);
-      }
-    const float mt = max_xor32(mx) * c;
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleLog2) != 0) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < S::kND; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      mt[nb] = max_xor32(mx) * c;
+      grow = grow || (mt[nb] > m_run[nb] + kRescaleLog2);
     }
-    const float neg_m = -m_run;
-
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short dependency chains
-    u32x4 pop[4];  // P^T B operands, one per 16-key slice
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+      for (int nb = 0; nb < NB; ++nb) {
+        const float m_new = fmaxf(m_run[nb], mt[nb]);
+        const float alpha = fast_exp2(m_run[nb] - m_new);
+        m_run[nb] = m_new;
+        l_run[nb] *= alpha;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        float e[8];
+        for (int db = 0; db < S::kND; ++db)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          e[i] = fast_exp2(__builtin_fmaf(s[sb][8 * half + i], c, neg_m));
-          rs[i & 3] += e[i];
-        }
-        u32x4 pk;
-        pk[0] = pack_bf16x2(e[0], e[1]);
-        pk[1] = pack_bf16x2(e[2], e[3]);
-        pk[2] = pack_bf16x2(e[4], e[5]);
-        pk[3] = pack_bf16x2(e[6], e[7]);
-        pop[2 * sb + half] = pk;
+          for (int r = 0; r < 16; ++r) oacc[nb][db][r] *= alpha;
       }
-    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    }
+
+    u32x4 pop[NB][4];  // P^T B operands, one per 16-key slice
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float neg_m = -m_run[nb];
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short dependency chains
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          float e[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            e[i] = fast_exp2(__builtin_fmaf(s[nb][sb][8 * half + i], c, neg_m));
+            rs[i & 3] += e[i];
+          }
+          u32x4 pk;
+          pk[0] = pack_bf16x2(e[0], e[1]);
+          pk[1] = pack_bf16x2(e[2], e[3]);
+          pk[2] = pack_bf16x2(e[4], e[5]);
+          pk[3] = pack_bf16x2(e[6], e[7]);
+          pop[nb][2 * sb + half] = pk;
+        }
+      l_run[nb] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    }
 
 #pragma unroll
-    for (int db = 0; db < S::kND; ++db) {
-      const int d = 32 * db + lq;
-      const uint16_t* vrow = vl + d * S::kVPitch;
-      const int sw = (d >> 3) & 7;
+    for (int db = 0; db < S::kND; ++db)
 #pragma unroll
       for (int cs = 0; cs < 4; ++cs) {
-        const int grp = (2 * cs + g) ^ sw;
-        const u32x4 a = *reinterpret_cast<const u32x4*>(vrow + 8 * grp);
-        oacc[db] = mfma32(a, pop[cs], oacc[db]);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(vb + (32 * db * S::kVPitch + 16 * cs) * 2);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) oacc[nb][db] = mfma32(a, pop[nb][cs], oacc[nb][db]);
       }
-    }
   };
 
   if (n_tiles > 0) {
@@ -340,45 +400,47 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdParams p) {
   // Tiles that need no mask for any wave of the workgroup come first (one
   // code path per loop keeps the accumulators in place); the tail of the key
   // range and the diagonal tiles follow with the masked path.
-  int n_plain = min(n_tiles, p.Lk / S::kBC);
+  int n_plain = min(n_tiles, n_full);
   if (CAUSAL) n_plain = min(n_plain, (q0 + 1) / S::kBC);
   int t = 0;
   for (; t < n_plain; ++t) {
     if (t + 1 < n_tiles) load_tile(t + 1);
     __syncthreads();
-    const uint16_t* kl = lds + (t & 1) * S::kBufElems;
-    process(std::false_type{}, kl, kl + S::kKElems, t * S::kBC);
+    process(std::false_type{}, t & 1, t * S::kBC);
     if (t + 1 < n_tiles) store_tile((t + 1) & 1);
   }
   for (; t < n_tiles; ++t) {
     if (t + 1 < n_tiles) load_tile(t + 1);
     __syncthreads();
     const int kv0 = t * S::kBC;
-    const uint16_t* kl = lds + (t & 1) * S::kBufElems;
-    if (!CAUSAL || kv0 <= wave_last_row) process(std::true_type{}, kl, kl + S::kKElems, kv0);
+    if (!CAUSAL || kv0 <= wave_last_row) process(std::true_type{}, t & 1, kv0);
     if (t + 1 < n_tiles) store_tile((t + 1) & 1);
   }
 
   // ---- epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2 ----
-  const float l_tot = sum_xor32(l_run);
-  if (qrow < p.Lq) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)qrow * p.o_st;
 #pragma unroll
-    for (int db = 0; db < S::kND; ++db)
+  for (int nb = 0; nb < NB; ++nb) {
+    const float l_tot = sum_xor32(l_run[nb]);
+    if (qrow[nb] < p.Lq) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + b * p.o_sb + h * p.o_sh +
+                       (int64_t)qrow[nb] * p.o_st;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = 32 * db + 8 * j + 4 * g;
-        if (d < D) {
-          u32x2 w;
-          w[0] = pack_bf16x2(oacc[db][4 * j + 0] * inv, oacc[db][4 * j + 1] * inv);
-          w[1] = pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + d) = w;
+      for (int db = 0; db < S::kND; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = 32 * db + 8 * j + 4 * g;
+          if (d < D) {
+            u32x2 w;
+            w[0] = pack_bf16x2(oacc[nb][db][4 * j + 0] * inv, oacc[nb][db][4 * j + 1] * inv);
+            w[1] = pack_bf16x2(oacc[nb][db][4 * j + 2] * inv, oacc[nb][db][4 * j + 3] * inv);
+            *reinterpret_cast<u32x2*>(orow + d) = w;
+          }
         }
+      if (g == 0) {
+        const float lse = l_tot > 0.f ? (m_run[nb] + log2f(l_tot)) * kLn2 : kNegInf;
+        p.lse[((int64_t)b * p.Hq + h) * p.Lq + qrow[nb]] = lse;
       }
-    if (g == 0) {
-      const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
-      p.lse[((int64_t)b * p.Hq + h) * p.Lq + qrow] = lse;
     }
   }
 }
