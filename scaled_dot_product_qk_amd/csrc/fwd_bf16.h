@@ -310,6 +310,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams p) {
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[nb][sb][r] = 0.f;
+    // Matrix-core phases run at raised wave priority, so that of the two
+    // waves sharing a SIMD the one with products to issue goes first and the
+    // other's softmax fills the vector ALU meanwhile.
+    __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
@@ -318,6 +322,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) s[nb][sb] = mfma32(a, qop[nb][kc], s[nb][sb]);
       }
+    __builtin_amdgcn_s_setprio(0);
 
     // Tile max on the raw scores (the scale is positive).
     float mt[NB];
@@ -378,6 +383,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams p) {
       l_run[nb] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
     }
 
+    __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int db = 0; db < S::kND; ++db)
 #pragma unroll
@@ -386,6 +392,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) oacc[nb][db] = mfma32(a, pop[nb][cs], oacc[nb][db]);
       }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   if (n_tiles > 0) {
