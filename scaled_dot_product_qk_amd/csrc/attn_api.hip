@@ -185,16 +185,17 @@ extern "C" attn_status_t attn_validate_decode(const attn_decode_args_t* a) {
   if (!strides_ok(a->q_strides, 2, 2) || !strides_ok(a->o_strides, 2, 2) ||
       !strides_ok(a->k_strides, 3, 2) || !strides_ok(a->v_strides, 3, 2))
     return ATTN_ERR_LAYOUT;
-  if (a->Lmax > kI32Max || a->B > kGridYMax || a->B * a->Hq > kI32Max) return ATTN_ERR_UNSUPPORTED;
   const int64_t hgroups = (a->Hq / a->Hkv + kDecHeadsPerGroup - 1) / kDecHeadsPerGroup;
-  if (a->Hkv * hgroups > kGridYMax) return ATTN_ERR_UNSUPPORTED;
+  if (a->Lmax > kI32Max || decode_chunks(a->Lmax) > kGridYMax || a->B * a->Hq > kI32Max ||
+      a->B * a->Hkv * hgroups > kI32Max)
+    return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 
 template <int D>
 static attn_status_t launch_decode(const DecodeParams& p, int B, hipStream_t s) {
   if (p.n_chunks > 0) {
-    hipLaunchKernelGGL(attn_decode_split_kernel<D>, dim3(p.n_chunks, p.Hkv * p.n_hgroups, B),
+    hipLaunchKernelGGL(attn_decode_split_kernel<D>, dim3(B * p.Hkv * p.n_hgroups, p.n_chunks),
                        dim3(256), 0, s, p);
     if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
   }

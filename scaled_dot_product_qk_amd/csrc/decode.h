@@ -56,6 +56,10 @@ struct DecodeParams {
   float scale_log2;
 };
 
+// Same threshold as the prefill kernels: the output is rescaled only when a
+// query's running max grows by more than 2^8.
+constexpr float kDecRescaleLog2 = 8.0f;
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeParams p) {
   static_assert(D % 32 == 0 && D <= 128, "decode head_dim must be 32, 64, 96 or 128");
@@ -64,10 +68,14 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeParams p) 
   __shared__ float red_l[kDecWaves][16];
   __shared__ float red_o[kDecWaves][16][D + 1];
 
-  const int chunk = blockIdx.x;
-  const int hkv = blockIdx.y / p.n_hgroups;
-  const int hg = blockIdx.y - hkv * p.n_hgroups;
-  const int b = blockIdx.z;
+  // Dispatch order: all (sequence, kv head, head group) units of chunk 0
+  // first, then chunk 1, ...; the chunks beyond short sequences, which exit at
+  // once, come last.
+  const int unit = blockIdx.x;
+  const int chunk = blockIdx.y;
+  const int hg = unit % p.n_hgroups;
+  const int hkv = (unit / p.n_hgroups) % p.Hkv;
+  const int b = unit / (p.n_hgroups * p.Hkv);
   int L = p.seqlens[b];
   L = L < 0 ? 0 : (L > p.Lmax ? p.Lmax : L);
   const int c0 = chunk * kDecChunk;
@@ -96,6 +104,26 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeParams p) 
 
   const int w0 = c0 + wave * kDecWaveSlots;
   const int w1 = min(w0 + kDecWaveSlots, L);
+  const int last = w1 - 1;  // slots beyond it are read from it (in bounds) and masked
+
+  // K rows as the A operand of S^T: lane row n of 16-key block kb.
+  auto load_k = [&](int base, u32x4 (&kr)[2][KC]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint16_t* row = kg + (int64_t)min(base + 16 * kb + n, last) * p.k_st;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) kr[kb][kc] = load16(row + 8 * (4 * kc + g));
+    }
+  };
+  // V rows for the transposed A operand: lane (n, g) loads 8 rows, head_dim
+  // chunk n (lanes with 8n >= D load nothing).
+  auto load_v = [&](int base, u32x4 (&vr)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int key = min(base + 16 * (i >> 2) + 4 * g + (i & 3), last);
+      vr[i] = (8 * n < D) ? load16(vg + (int64_t)key * p.v_st + 8 * n) : zero16();
+    }
+  };
 
   f32x4 oacc[8];
 #pragma unroll
@@ -103,22 +131,23 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeParams p) 
 #pragma unroll
     for (int r = 0; r < 4; ++r) oacc[t][r] = 0.f;
   float m_run = kNegInf, l_run = 0.f;
+  const float c = p.scale_log2;
 
+  u32x4 kreg[2][KC];
+  u32x4 vreg[8];
+  if (w0 < w1) {
+    // Q must have landed first so that waits for it do not also wait for
+    // the cache rows issued below.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    load_k(w0, kreg);
+    load_v(w0, vreg);
+  }
+
+  // Each step's loads for the next 32 keys are issued as soon as the
+  // registers they land in have been consumed, so cache rows stay in flight
+  // while this step computes.
   for (int base = w0; base < w1; base += 32) {
-    u32x4 kreg[2][KC];
-    u32x4 vreg[8];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = base + 16 * kb + n;
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-        kreg[kb][kc] = key < w1 ? load16(kg + (int64_t)key * p.k_st + 8 * (4 * kc + g)) : zero16();
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int key = base + 16 * (i >> 2) + 4 * g + (i & 3);
-      vreg[i] = (key < w1 && 8 * n < D) ? load16(vg + (int64_t)key * p.v_st + 8 * n) : zero16();
-    }
+    const int nxt = base + 32;
 
     // S^T (16 keys x 16 query columns) for the two 16-key blocks.
     f32x4 s[2];
@@ -129,6 +158,7 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeParams p) 
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) s[kb] = mfma16(kreg[kb][kc], qop[kc], s[kb]);
     }
+    if (nxt < w1) load_k(nxt, kreg);
 
     float mx = kNegInf;
 #pragma unroll
@@ -136,23 +166,30 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeParams p) 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = base + 16 * kb + 4 * g + r;
-        const float x = key < w1 ? s[kb][r] * p.scale_log2 : kNegInf;
+        const float x = key < w1 ? s[kb][r] * c : kNegInf;
         s[kb][r] = x;
         mx = fmaxf(mx, x);
       }
     mx = max_xor32(max_xor16(mx));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kDecRescaleLog2) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oacc[t][r] *= alpha;
+    }
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        s[kb][r] = fast_exp2(s[kb][r] - m_new);
+        s[kb][r] = fast_exp2(s[kb][r] - m_run);
         rs += s[kb][r];
       }
-    l_run = l_run * alpha + rs;
+    l_run += rs;
     // P^T B operand: k slot (g, i) is key base + 16*(i/4) + 4*g + i%4.
     u32x4 pop;
     pop[0] = pack_bf16x2(s[0][0], s[0][1]);
@@ -160,20 +197,18 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeParams p) 
     pop[2] = pack_bf16x2(s[1][0], s[1][1]);
     pop[3] = pack_bf16x2(s[1][2], s[1][3]);
 
+    // A operands of the 8 products: lane row n is head_dim 8n + t, k slot
+    // (g, i) the key of vreg[i]; element t of each loaded row, paired by key.
+    u32x4 a[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < 8; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) oacc[t][r] *= alpha;
-      // A operand of product t: lane row n is head_dim 8n + t, k slot (g, i)
-      // the key of vreg[i]; element t of each loaded row, paired by key.
-      u32x4 a;
+      for (int j = 0; j < 4; ++j)
+        a[t][j] = __builtin_amdgcn_perm(vreg[2 * j + 1][t >> 1], vreg[2 * j][t >> 1],
+                                        (t & 1) ? 0x07060302u : 0x05040100u);
+    if (nxt < w1) load_v(nxt, vreg);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = vreg[2 * j][t >> 1], hi = vreg[2 * j + 1][t >> 1];
-        a[j] = (t & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-      }
-      oacc[t] = mfma16(a, pop, oacc[t]);
-    }
+    for (int t = 0; t < 8; ++t) oacc[t] = mfma16(a[t], pop, oacc[t]);
   }
 
   // Combine the 4 waves' partial results in LDS.
@@ -223,18 +258,34 @@ __global__ __launch_bounds__(D) void attn_decode_merge_kernel(DecodeParams p) {
   const int ns = (L + kDecChunk - 1) / kDecChunk;
   const int64_t row0 = (int64_t)bh * p.n_chunks;
 
-  float M = kNegInf;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, p.lse_part[row0 + s]);
-  float wsum = 0.f, acc = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = expf(p.lse_part[row0 + s] - M);
-    wsum += w;
-    acc += w * p.o_part[(row0 + s) * D + d];
+  // Up to 16 chunks per pass, their loads issued together; the running max
+  // and sums are rescaled between passes.
+  float M = kNegInf, wsum = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += 16) {
+    float lsv[16], ov[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const bool ok = s0 + j < ns;
+      lsv[j] = ok ? p.lse_part[row0 + s0 + j] : kNegInf;
+      ov[j] = ok ? p.o_part[(row0 + s0 + j) * D + d] : 0.f;
+    }
+    float Mc = M;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) Mc = fmaxf(Mc, lsv[j]);
+    const float sc = expf(M - Mc);  // first pass: exp(-inf) = 0 on zero sums
+    wsum *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float w = expf(lsv[j] - Mc);
+      wsum += w;
+      acc += w * ov[j];
+    }
+    M = Mc;
   }
   const float o = ns > 0 ? acc / wsum : 0.f;
   uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + b * p.o_sb + (int64_t)h * p.o_sh;
-  // bf16 round-to-nearest-even of one value.
-  orow[d] = (uint16_t)(pack_bf16x2(o, 0.f) & 0xffffu);
+  orow[d] = (uint16_t)(pack_bf16x2(o, 0.f) & 0xffffu);  // bf16, round-to-nearest-even
   if (d == 0) p.lse[bh] = ns > 0 ? M + logf(wsum) : kNegInf;
 }
 

@@ -145,7 +145,7 @@ def test_decode_valid(d, Hq, Hkv):
     (dict(Hkv=3), SHAPE), (dict(Hkv=0), SHAPE), (dict(Lmax=-1), SHAPE),
     (dict(scale=float("nan")), SHAPE),
     (dict(q=P + 2), LAYOUT), (dict(seqlens=P + 2), LAYOUT), (dict(ks=(8 * 1000 * 128, 1000 * 128, 130)), LAYOUT),
-    (dict(B=70000), UNSUP),
+    (dict(Lmax=40_000_000), UNSUP), (dict(Lmax=2 ** 31), UNSUP),
 ])
 def test_decode_rejections(kw, status):
     assert vdec(**kw) == status
