@@ -197,18 +197,19 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeParams p) 
     pop[2] = pack_bf16x2(s[1][0], s[1][1]);
     pop[3] = pack_bf16x2(s[1][2], s[1][3]);
 
-    // A operands of the 8 products: lane row n is head_dim 8n + t, k slot
-    // (g, i) the key of vreg[i]; element t of each loaded row, paired by key.
-    u32x4 a[8];
+    // A operand of product t: lane row n is head_dim 8n + t, k slot (g, i)
+    // the key of vreg[i]; element t of each loaded row, paired by key.  Each
+    // operand is built right before its product, so only one is live.
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < 8; ++t) {
+      u32x4 a;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        a[t][j] = __builtin_amdgcn_perm(vreg[2 * j + 1][t >> 1], vreg[2 * j][t >> 1],
-                                        (t & 1) ? 0x07060302u : 0x05040100u);
+        a[j] = __builtin_amdgcn_perm(vreg[2 * j + 1][t >> 1], vreg[2 * j][t >> 1],
+                                     (t & 1) ? 0x07060302u : 0x05040100u);
+      oacc[t] = mfma16(a, pop, oacc[t]);
+    }
     if (nxt < w1) load_v(nxt, vreg);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) oacc[t] = mfma16(a[t], pop, oacc[t]);
   }
 
   // Combine the 4 waves' partial results in LDS.
