@@ -61,7 +61,7 @@ struct DecodeParams {
 constexpr float kDecRescaleLog2 = 8.0f;
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, 3) void attn_decode_split_kernel(DecodeParams p) {
   static_assert(D % 32 == 0 && D <= 128, "decode head_dim must be 32, 64, 96 or 128");
   constexpr int KC = D / 32;      // k-slices of S^T = K Q^T
   __shared__ float red_m[kDecWaves][16];
@@ -76,11 +76,6 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeParams p) 
   const int hg = unit % p.n_hgroups;
   const int hkv = (unit / p.n_hgroups) % p.Hkv;
   const int b = unit / (p.n_hgroups * p.Hkv);
-  int L = p.seqlens[b];
-  L = L < 0 ? 0 : (L > p.Lmax ? p.Lmax : L);
-  const int c0 = chunk * kDecChunk;
-  if (c0 >= L) return;  // whole workgroup leaves together
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -91,6 +86,8 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeParams p) 
   const bool hvalid = hidx < p.group;
   const int h = hkv * p.group + hidx;
 
+  // The length and the queries are loaded together (Q does not depend on it).
+  int L = p.seqlens[b];
   // Q^T B operand: k slot (g, i) of slice kc is head_dim index 8*(4*kc + g) + i.
   u32x4 qop[KC];
   {
@@ -98,6 +95,9 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeParams p) 
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) qop[kc] = hvalid ? load16(qr + 8 * (4 * kc + g)) : zero16();
   }
+  L = L < 0 ? 0 : (L > p.Lmax ? p.Lmax : L);
+  const int c0 = chunk * kDecChunk;
+  if (c0 >= L) return;  // whole workgroup leaves together
 
   const uint16_t* kg = reinterpret_cast<const uint16_t*>(p.k) + b * p.k_sb + hkv * p.k_sh;
   const uint16_t* vg = reinterpret_cast<const uint16_t*>(p.v) + b * p.v_sb + hkv * p.v_sh;
