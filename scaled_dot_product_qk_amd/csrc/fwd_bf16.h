@@ -125,13 +125,17 @@ __device__ __forceinline__ int vt_pos16(int kk) {
   return ((kk >> 2) & 1) * 8 + (kk >> 3) * 4 + (kk & 3);
 }
 
-// Row maxima are tracked in the log2 domain of the scaled scores.  The output
-// and the normaliser are rescaled only when some row's tile maximum exceeds
-// the reference maximum by more than this many binary orders (a wave-uniform
-// decision); otherwise the probabilities are formed against the stale
-// reference and stay below 2^kRescaleLog2, well inside fp32 and bf16 range.
-// LSE = ref + log2(l) is exact either way.
+// Row maxima are tracked in the log2 domain of the scaled scores, as a
+// reference m that only moves when it must.  Each tile's probabilities are
+// first formed against the current m; only if some lane's share of the tile
+// sum exceeds 2^kRescaleLog2 (or is not a number, as before a row's first
+// tile, where m is still -inf) does the wave take the tile max, move m,
+// rescale O and l, and form the probabilities again.  Every probability
+// therefore stays below 2^kRescaleLog2, well inside fp32 and bf16 range, and
+// LSE = m + log2(l) is exact for any m.
 constexpr float kRescaleLog2 = 8.0f;
+constexpr float kSumGuard = 256.f;
+static_assert(kSumGuard == float(1 << int(kRescaleLog2)), "guard is 2^kRescaleLog2");
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams p) {
@@ -324,43 +328,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams p) {
       }
     __builtin_amdgcn_s_setprio(0);
 
-    // Tile max on the raw scores (the scale is positive).
-    float mt[NB];
-    bool grow = false;
+    if constexpr (MASK) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      float mx = kNegInf;
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+        for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if constexpr (MASK) {
+          for (int r = 0; r < 16; ++r) {
             const int key = kv0 + 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3);
             const bool vis = key < p.Lk && (!CAUSAL || key <= qrow[nb]);
             s[nb][sb][r] = vis ? s[nb][sb][r] : kNegInf;
           }
-          mx = fmaxf(mx, s[nb][sb][r]);
-        }
-      mt[nb] = max_xor32(mx) * c;
-      grow = grow || (mt[nb] > m_run[nb] + kRescaleLog2);
-    }
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const float m_new = fmaxf(m_run[nb], mt[nb]);
-        const float alpha = fast_exp2(m_run[nb] - m_new);
-        m_run[nb] = m_new;
-        l_run[nb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < S::kND; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[nb][db][r] *= alpha;
-      }
     }
 
-    u32x4 pop[NB][4];  // P^T B operands, one per 16-key slice
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+    // P = exp2(c s - m) for row block nb, packed as the P^T B operands; returns
+    // this lane's share of the row sum.
+    u32x4 pop[NB][4];
+    auto exp_pack = [&](int nb) {
       const float neg_m = -m_run[nb];
       float rs[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short dependency chains
 #pragma unroll
@@ -380,7 +364,28 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams p) {
           pk[3] = pack_bf16x2(e[6], e[7]);
           pop[nb][2 * sb + half] = pk;
         }
-      l_run[nb] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+      return (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    };
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float lsum = exp_pack(nb);
+      if (__builtin_amdgcn_ballot_w64(!(lsum <= kSumGuard)) != 0) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][sb][r]);
+        const float m_new = fmaxf(m_run[nb], max_xor32(mx) * c);  // the scale is positive
+        const float alpha = m_new == m_run[nb] ? 1.f : fast_exp2(m_run[nb] - m_new);
+        m_run[nb] = m_new;
+        l_run[nb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < S::kND; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[nb][db][r] *= alpha;
+        lsum = exp_pack(nb);
+      }
+      l_run[nb] += lsum;
     }
 
     __builtin_amdgcn_s_setprio(2);
