@@ -103,26 +103,48 @@ struct Bf16FwdShape {
   static constexpr int kKC = D / 16;                 // k-slices of the Q K^T product
   static constexpr int kDP = (D + 31) / 32 * 32;     // rows of O^T padded to 32
   static constexpr int kND = kDP / 32;               // 32-row blocks of O^T
-  static constexpr int kChunks = D / 8;              // 16-byte chunks per row
-  static constexpr int kKPitch = D + 8;              // K row pitch in LDS (elements)
-  static constexpr int kVPitch = kBC + 8;            // V^T row pitch in LDS (elements)
-  static constexpr int kKElems = kBC * kKPitch;
-  static constexpr int kVElems = kDP * kVPitch;
-  static constexpr int kBufBytes = (kKElems + kVElems) * 2;
-  static constexpr int kLdsBytes = 2 * kBufBytes;
-  static constexpr int kKItems = kBC * kChunks;         // 16-byte K loads per tile
-  static constexpr int kVItems = (kBC / 2) * kChunks;   // (key pair, chunk) V loads
-  static constexpr int kKIter = (kKItems + 255) / 256;
-  static constexpr int kVIter = (kVItems + 255) / 256;
+  static constexpr int kChunks = D / 8;              // 16-byte chunks of a row in memory
+  static constexpr int kPitch = D <= 64 ? 8 : 16;    // 16-byte chunks of a row in LDS
+  static constexpr int kRowBytes = 16 * kPitch;
+  static constexpr int kTileBytes = kBC * kRowBytes;
+  static constexpr int kBufBytes = 2 * kTileBytes;  // K tile, then V tile
+  static constexpr int kLdsBytes = 2 * kBufBytes;   // double buffered
+  static constexpr int kRowsPerCopy = 64 / kPitch;  // rows one 1 KB copy instruction fills
+  static constexpr int kCopies = 2 * kBC / kRowsPerCopy;  // per tile, K then V
+  static constexpr int kCopiesPerWave = kCopies / kWaves;
+  static constexpr int kKVar = kPitch == 8 ? 2 : 4;  // K swizzle patterns across one wave's copies
   static_assert(D % 16 == 0, "head_dim must be a multiple of 16");
+  static_assert(kChunks <= kPitch && 2 * kDP <= kRowBytes, "a padded row must fit its LDS pitch");
+  static_assert(kCopiesPerWave % kKVar == 0 && 2 * kCopiesPerWave * kRowsPerCopy == kBC,
+                "each wave copies whole swizzle periods of one of the two tiles");
   static_assert(kBufBytes < 65536, "in-buffer LDS offsets must fit the instruction offset field");
 };
 
-// Position of key kk (0..15) of a 16-key slice inside V^T's LDS row: the
-// score accumulator gives lane half g the keys {4g..4g+3, 8+4g..8+4g+3} of a
-// slice, stored contiguously at 8g..8g+7.
-__device__ __forceinline__ int vt_pos16(int kk) {
-  return ((kk >> 2) & 1) * 8 + (kk >> 3) * 4 + (kk & 3);
+// LDS layout of a key row: its 16-byte chunks are XOR-swizzled by the row
+// index so that the operand reads spread over all banks.
+//   K (A operand of S^T = K Q^T, 16 bytes of 32 consecutive rows per read):
+//     8-chunk rows: c ^ (r & 7) ^ ((r >> 3) & 1); 16-chunk rows: c ^ (r & 15).
+//     Any 8 consecutive rows at one logical chunk use 8 different chunks, and
+//     any 16 use 16 different (row parity, chunk) bank groups.
+//   V (read with ds_read_b64_tr_b16, 32 bytes of 4 consecutive rows per
+//     16-lane group): the 32-byte halves are XOR-ed by r & 3, which puts the 4
+//     rows in 4 different bank groups.
+template <int PITCH>
+__device__ __forceinline__ int fwd_k_swz(int r) {
+  return PITCH == 8 ? (r & 7) ^ ((r >> 3) & 1) : (r & 15);
+}
+template <int PITCH>
+__device__ __forceinline__ int fwd_v_swz(int r) {
+  return (PITCH / 4) * (r & 3);
+}
+
+// 16 bytes per lane from global memory into LDS at lds_base + 16 * lane
+// (lds_base wave-uniform).  Inline assembly, so that the compiler neither
+// counts the copy among its outstanding loads nor makes LDS reads and barriers
+// wait for it: the kernel waits for its copies itself (vmcnt) before the
+// barrier that publishes them.
+__device__ __forceinline__ void fwd_copy16(const void* src, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_base) : "memory");
 }
 
 // Row maxima are tracked in the log2 domain of the scaled scores, as a
@@ -141,12 +163,14 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams p) {
   using S = Bf16FwdShape<D>;
   constexpr int NB = S::kNB;
+  typedef __attribute__((address_space(3))) char lds_char;
+  typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  char* const lds_b = reinterpret_cast<char*>(lds);
+  lds_char* const lds_b = (lds_char*)(lds);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31;  // query column within a 32-query block (n index)
   const int g = lane >> 5;   // lane half
 
@@ -187,105 +211,77 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams p) {
   const int n_full = p.Lk / S::kBC;  // tiles with no key beyond Lk
   const int wave_last_row = row0 + S::kRowsPerWave - 1;
 
-  // Zero the padded rows of V^T (head_dim not a multiple of 32) once; the
-  // loader never writes them and their products land in discarded O^T rows.
-  if (S::kDP != D) {
-    for (int i = tid; i < (S::kDP - D) * S::kVPitch; i += 256) {
-      lds[S::kKElems + D * S::kVPitch + i] = 0;
-      lds[S::kBufBytes / 2 + S::kKElems + D * S::kVPitch + i] = 0;
-    }
-  }
-
-  // ---- per-thread loader plan ----
-  // K: item -> (key row, 16-byte chunk), chunk fastest (coalesced rows).
-  // V: item -> (key pair, chunk), key pair fastest, so that the 4-byte V^T
-  //    writes of one instruction hit 32 different LDS banks.
-  int64_t koff[S::kKIter];
-  int kst[S::kKIter];
-  int64_t voff[S::kVIter];
-  int vst[S::kVIter];
+  // ---- tile copies: global memory straight into LDS, no registers ----
+  // Copy instruction ci of a tile fills kRowsPerCopy rows (1 KB, lane l ->
+  // row l / kPitch, physical chunk l % kPitch) of the K tile (first half of
+  // the ci range) or the V tile; wave w issues kCopiesPerWave consecutive
+  // ones, so waves 0-1 copy K and waves 2-3 copy V.  Each lane fetches the
+  // logical chunk its slot holds; slots of padding chunks (head_dim 80) stay
+  // idle.  Per-lane offsets repeat with period kKVar copies.
+  constexpr int kHalfCopies = S::kCopies / 2;
+  const bool copies_k = wave < S::kWaves / 2;
+  const uint16_t* cp_src = copies_k ? kg : vg;
+  const int64_t cp_st = copies_k ? p.k_st : p.v_st;
+  const int cp_row = lane / S::kPitch;  // row within one copy
+  const int cp_row0 = S::kRowsPerCopy * ((wave % (S::kWaves / 2)) * S::kCopiesPerWave);
+  const uint32_t cp_lds0 = (uint32_t)(uintptr_t)lds_b + (copies_k ? 0 : S::kTileBytes) + cp_row0 * S::kRowBytes;
+  int cp_chunk8[S::kKVar];   // 8 x logical chunk
+  int64_t cp_off[S::kKVar];  // element offset of the lane's chunk within its copy
+  bool cp_on[S::kKVar];
 #pragma unroll
-  for (int it = 0; it < S::kKIter; ++it) {
-    const int item = tid + 256 * it;
-    const int row = item / S::kChunks, ch = item - (item / S::kChunks) * S::kChunks;
-    koff[it] = (int64_t)row * p.k_st + 8 * ch;
-    kst[it] = (row * S::kKPitch + 8 * ch) * 2;
+  for (int v = 0; v < S::kKVar; ++v) {
+    const int r = S::kRowsPerCopy * v + cp_row;  // row index modulo the swizzle period
+    const int pc = lane % S::kPitch;
+    const int lc = pc ^ (copies_k ? fwd_k_swz<S::kPitch>(r) : fwd_v_swz<S::kPitch>(r));
+    cp_chunk8[v] = 8 * lc;
+    cp_off[v] = (int64_t)cp_row * cp_st + 8 * lc;
+    cp_on[v] = lc < S::kChunks;
   }
-#pragma unroll
-  for (int it = 0; it < S::kVIter; ++it) {
-    const int item = tid + 256 * it;
-    const int pr = item & 31, ch = item >> 5;
-    const int key = 2 * pr;
-    voff[it] = (int64_t)key * p.v_st + 8 * ch;
-    vst[it] = S::kKElems * 2 + (8 * ch * S::kVPitch + (key & ~15) + vt_pos16(key & 15)) * 2;
-  }
-
-  u32x4 kreg[S::kKIter] = {};
-  u32x4 vreg[S::kVIter][2] = {};
-
-  // Full tiles load without checks; the tile holding key Lk - 1 reads rows
+  // Full tiles copy without checks; the tile holding key Lk - 1 reads rows
   // beyond it from row Lk - 1 instead (in bounds and finite), and those keys
   // are masked to -inf, so they carry weight 0.
-  auto load_tile = [&](int t) {
+  auto issue_tile = [&](int t) {
     const int kv0 = t * S::kBC;
+    const uint32_t dst = cp_lds0 + (t & 1) * S::kBufBytes;
     if (t < n_full) {
-      const uint16_t* kt = kg + (int64_t)kv0 * p.k_st;
-      const uint16_t* vt = vg + (int64_t)kv0 * p.v_st;
 #pragma unroll
-      for (int it = 0; it < S::kKIter; ++it)
-        if (S::kKItems % 256 == 0 || tid + 256 * it < S::kKItems) kreg[it] = load16(kt + koff[it]);
-#pragma unroll
-      for (int it = 0; it < S::kVIter; ++it)
-        if (S::kVItems % 256 == 0 || tid + 256 * it < S::kVItems) {
-          vreg[it][0] = load16(vt + voff[it]);
-          vreg[it][1] = load16(vt + voff[it] + p.v_st);
-        }
+      for (int j = 0; j < S::kCopiesPerWave; ++j) {
+        const uint16_t* src = cp_src + (int64_t)(kv0 + cp_row0 + S::kRowsPerCopy * j) * cp_st;
+        if (S::kChunks == S::kPitch || cp_on[j % S::kKVar])
+          fwd_copy16(src + cp_off[j % S::kKVar], dst + j * S::kRowsPerCopy * S::kRowBytes);
+      }
     } else {
       const int last = p.Lk - 1;
 #pragma unroll
-      for (int it = 0; it < S::kKIter; ++it) {
-        const int item = tid + 256 * it;
-        if (S::kKItems % 256 == 0 || item < S::kKItems) {
-          const int row = item / S::kChunks, ch = item - (item / S::kChunks) * S::kChunks;
-          kreg[it] = load16(kg + (int64_t)min(kv0 + row, last) * p.k_st + 8 * ch);
-        }
-      }
-#pragma unroll
-      for (int it = 0; it < S::kVIter; ++it) {
-        const int item = tid + 256 * it;
-        if (S::kVItems % 256 == 0 || item < S::kVItems) {
-          const int pr = item & 31, ch = item >> 5;
-          vreg[it][0] = load16(vg + (int64_t)min(kv0 + 2 * pr, last) * p.v_st + 8 * ch);
-          vreg[it][1] = load16(vg + (int64_t)min(kv0 + 2 * pr + 1, last) * p.v_st + 8 * ch);
-        }
+      for (int j = 0; j < S::kCopiesPerWave; ++j) {
+        const int key = min(kv0 + cp_row0 + S::kRowsPerCopy * j + cp_row, last);
+        if (S::kChunks == S::kPitch || cp_on[j % S::kKVar])
+          fwd_copy16(cp_src + (int64_t)key * cp_st + cp_chunk8[j % S::kKVar],
+                     dst + j * S::kRowsPerCopy * S::kRowBytes);
       }
     }
   };
 
-  auto store_tile = [&](int buf) {
-    char* base = lds_b + buf * S::kBufBytes;
+  // ---- LDS operand offsets (bytes within a buffer) ----
+  // K A operand of slice kc: row lq (+32 per key half), logical chunk 2 kc + g.
+  // The swizzle only flips chunk bits, so slice kc's offset is slice 0's with
+  // bits 5 and up flipped by kc.
+  const int k_rd = lq * S::kRowBytes + 16 * (fwd_k_swz<S::kPitch>(lq) ^ g);
+  // V^T A operand of d-block db, 16-key slice cs, from two transposing reads:
+  // lane (G = lane / 16, i = lane % 16 / 4, q = lane % 4) points at key row
+  // 16 cs + 4 g + i (+ 8 for the second read), head_dim 32 db + 16 (G & 1) +
+  // 4 q, and receives that head_dim index of keys 16 cs + 4 g + 0..3 (+ 8):
+  // the key order of the score accumulator's rows, i.e. of P's B operand.
+  int v_rd[S::kND];
+  {
+    const int G = lane >> 4, i = (lane & 15) >> 2, q = lane & 3;
 #pragma unroll
-    for (int it = 0; it < S::kKIter; ++it)
-      if (S::kKItems % 256 == 0 || tid + 256 * it < S::kKItems)
-        *reinterpret_cast<u32x4*>(base + kst[it]) = kreg[it];
-#pragma unroll
-    for (int it = 0; it < S::kVIter; ++it)
-      if (S::kVItems % 256 == 0 || tid + 256 * it < S::kVItems) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          // (key, key + 1) pair of head_dim element 8*ch + t: low or high
-          // halves of the two rows' words.
-          const uint32_t w = __builtin_amdgcn_perm(vreg[it][1][t >> 1], vreg[it][0][t >> 1],
-                                                   (t & 1) ? 0x07060302u : 0x05040100u);
-          *reinterpret_cast<uint32_t*>(base + vst[it] + t * S::kVPitch * 2) = w;
-        }
-      }
-  };
-
-  // Per-lane LDS read bases: K rows lq (+32 per key block), V^T rows lq (+32
-  // per head_dim block); every other offset is a compile-time constant.
-  const int k_rd = (lq * S::kKPitch + 8 * g) * 2;
-  const int v_rd = S::kKElems * 2 + (lq * S::kVPitch + 8 * g) * 2;
+    for (int db = 0; db < S::kND; ++db) {
+      const int d0 = 32 * db + 16 * (G & 1) + 4 * q;  // 4 elements within one chunk
+      v_rd[db] = S::kTileBytes + (4 * g + i) * S::kRowBytes +
+                 16 * ((d0 >> 3) ^ fwd_v_swz<S::kPitch>(i)) + 2 * (d0 & 7);
+    }
+  }
 
   f32x16 oacc[NB][S::kND];
 #pragma unroll
@@ -303,130 +299,173 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams p) {
 
   // One key tile: S^T, online softmax, O^T += V^T P^T.  MASK selects the
   // variant that masks keys beyond Lk and (causal) keys after the query.
+  //
+  // The tile is taken as two 32-key halves so that each wave keeps its matrix
+  // core and its vector ALU busy at once: the products of one half are issued
+  // interleaved with the softmax of the other,
+  //
+  //   S(h0) | S(h1) + softmax(h0) | O += P(h0) V(h0) + softmax(h1) | O += P(h1) V(h1)
+  //
+  // which is possible because the probabilities of a half depend only on its
+  // own scores and the reference max (see kSumGuard): each half has its own
+  // guard, and a rescale of O after the first half's products is exact.
   auto process = [&](auto mask_tag, int buf, int kv0) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const char* kb = lds_b + buf * S::kBufBytes + k_rd;
-    const char* vb = lds_b + buf * S::kBufBytes + v_rd;
+    const lds_char* kb = lds_b + buf * S::kBufBytes;
+    lds_char* vb = lds_b + buf * S::kBufBytes;
     f32x16 s[NB][2];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[nb][sb][r] = 0.f;
-    // Matrix-core phases run at raised wave priority, so that of the two
-    // waves sharing a SIMD the one with products to issue goes first and the
-    // other's softmax fills the vector ALU meanwhile.
-    __builtin_amdgcn_s_setprio(2);
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int kc = 0; kc < S::kKC; ++kc) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kb + (32 * sb * S::kKPitch + 16 * kc) * 2);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) s[nb][sb] = mfma32(a, qop[nb][kc], s[nb][sb]);
-      }
-    __builtin_amdgcn_s_setprio(0);
+    u32x4 pop[NB][4];  // P^T B operands, one per 16-key slice
 
-    if constexpr (MASK) {
+    auto read_k = [&](int sb, u32x4 (&ka)[S::kKC]) {
+#pragma unroll
+      for (int kc = 0; kc < S::kKC; ++kc)
+        ka[kc] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            kb + (k_rd ^ (32 * kc)) + 32 * sb * S::kRowBytes);
+    };
+    auto read_v = [&](int sb, u32x4 (&va)[S::kND][2]) {
+#pragma unroll
+      for (int db = 0; db < S::kND; ++db)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          lds_char* a0 = vb + v_rd[db] + 16 * (2 * sb + j) * S::kRowBytes;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)a0);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(a0 + 8 * S::kRowBytes));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+          va[db][j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+        }
+    };
+    auto qk = [&](int sb, const u32x4 (&ka)[S::kKC]) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+        for (int r = 0; r < 16; ++r) s[nb][sb][r] = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < S::kKC; ++kc)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) s[nb][sb] = mfma32(ka[kc], qop[nb][kc], s[nb][sb]);
+    };
+    auto pv = [&](int sb, const u32x4 (&va)[S::kND][2]) {
+#pragma unroll
+      for (int db = 0; db < S::kND; ++db)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) oacc[nb][db] = mfma32(va[db][j], pop[nb][2 * sb + j], oacc[nb][db]);
+    };
+    // P = exp2(c s - m) for half sb of row block nb, packed as two P^T B
+    // operands; returns this lane's share of the half's row sum.
+    auto exp_half = [&](int sb, int nb) {
+      const float neg_m = -m_run[nb];
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};  // short dependency chains
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          e[i] = fast_exp2(__builtin_fmaf(s[nb][sb][8 * half + i], c, neg_m));
+          rs[i & 3] += e[i];
+        }
+        u32x4 pk;
+        pk[0] = pack_bf16x2(e[0], e[1]);
+        pk[1] = pack_bf16x2(e[2], e[3]);
+        pk[2] = pack_bf16x2(e[4], e[5]);
+        pk[3] = pack_bf16x2(e[6], e[7]);
+        pop[nb][2 * sb + half] = pk;
+      }
+      return (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    };
+    // Softmax of half sb.  N_MFMA products issued just before it are spread
+    // between its vector instructions.
+    auto softmax_half = [&](int sb, auto n_mfma_tag) {
+      constexpr int N_MFMA = decltype(n_mfma_tag)::value;
+      if constexpr (MASK) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kv0 + 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3);
             const bool vis = key < p.Lk && (!CAUSAL || key <= qrow[nb]);
             s[nb][sb][r] = vis ? s[nb][sb][r] : kNegInf;
           }
-    }
-
-    // P = exp2(c s - m) for row block nb, packed as the P^T B operands; returns
-    // this lane's share of the row sum.
-    u32x4 pop[NB][4];
-    auto exp_pack = [&](int nb) {
-      const float neg_m = -m_run[nb];
-      float rs[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short dependency chains
+      }
+      float ls[NB];
+      bool redo = false;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+      for (int nb = 0; nb < NB; ++nb) {
+        ls[nb] = exp_half(sb, nb);
+        redo = redo || !(ls[nb] <= kSumGuard);
+      }
+      // about 60 vector instructions per row block: one product per share
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          float e[8];
+      for (int i = 0; i < N_MFMA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 56 * NB / N_MFMA, 0);
+      }
+      if (__builtin_amdgcn_ballot_w64(redo) != 0) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            e[i] = fast_exp2(__builtin_fmaf(s[nb][sb][8 * half + i], c, neg_m));
-            rs[i & 3] += e[i];
-          }
-          u32x4 pk;
-          pk[0] = pack_bf16x2(e[0], e[1]);
-          pk[1] = pack_bf16x2(e[2], e[3]);
-          pk[2] = pack_bf16x2(e[4], e[5]);
-          pk[3] = pack_bf16x2(e[6], e[7]);
-          pop[nb][2 * sb + half] = pk;
-        }
-      return (rs[0] + rs[1]) + (rs[2] + rs[3]);
-    };
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      float lsum = exp_pack(nb);
-      if (__builtin_amdgcn_ballot_w64(!(lsum <= kSumGuard)) != 0) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+        for (int nb = 0; nb < NB; ++nb) {
+          float mx = kNegInf;
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][sb][r]);
-        const float m_new = fmaxf(m_run[nb], max_xor32(mx) * c);  // the scale is positive
-        const float alpha = m_new == m_run[nb] ? 1.f : fast_exp2(m_run[nb] - m_new);
-        m_run[nb] = m_new;
-        l_run[nb] *= alpha;
+          const float m_new = fmaxf(m_run[nb], max_xor32(mx) * c);  // the scale is positive
+          const float alpha = m_new == m_run[nb] ? 1.f : fast_exp2(m_run[nb] - m_new);
+          m_run[nb] = m_new;
+          l_run[nb] *= alpha;
 #pragma unroll
-        for (int db = 0; db < S::kND; ++db)
+          for (int db = 0; db < S::kND; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[nb][db][r] *= alpha;
-        lsum = exp_pack(nb);
+            for (int r = 0; r < 16; ++r) oacc[nb][db][r] *= alpha;
+          ls[nb] = exp_half(sb, nb);
+        }
       }
-      l_run[nb] += lsum;
-    }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) l_run[nb] += ls[nb];
+    };
 
+    constexpr int kQKMfma = S::kKC * NB, kPVMfma = S::kND * 2 * NB;
+    u32x4 ka0[S::kKC], ka1[S::kKC], va0[S::kND][2], va1[S::kND][2];
+    read_k(0, ka0);
+    read_k(1, ka1);
     __builtin_amdgcn_s_setprio(2);
-#pragma unroll
-    for (int db = 0; db < S::kND; ++db)
-#pragma unroll
-      for (int cs = 0; cs < 4; ++cs) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(vb + (32 * db * S::kVPitch + 16 * cs) * 2);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) oacc[nb][db] = mfma32(a, pop[nb][cs], oacc[nb][db]);
-      }
+    qk(0, ka0);
+    __builtin_amdgcn_s_setprio(0);
+    read_v(0, va0);
+    qk(1, ka1);
+    softmax_half(0, std::integral_constant<int, kQKMfma>{});
+    read_v(1, va1);
+    pv(0, va0);
+    softmax_half(1, std::integral_constant<int, kPVMfma>{});
+    __builtin_amdgcn_s_setprio(2);
+    pv(1, va1);
     __builtin_amdgcn_s_setprio(0);
   };
 
-  if (n_tiles > 0) {
-    // Q must have landed before the loop: the compiler's in-order view of
-    // outstanding loads would otherwise make the first use of Q inside the
-    // loop wait for the next tile's prefetch as well.
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-    load_tile(0);
-    store_tile(0);
-  }
+  // Q must have landed before the first copy: the copies are invisible to the
+  // compiler, and a later wait for Q would not know to let them run on.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  if (n_tiles > 0) issue_tile(0);
 
-  // Tiles that need no mask for any wave of the workgroup come first (one
-  // code path per loop keeps the accumulators in place); the tail of the key
+  // Iteration t: wait for this wave's copies of tile t, barrier (all copies
+  // of t are in LDS, and every wave is done with tile t - 1, whose buffer the
+  // copies of t + 1 then overwrite), copy t + 1, process t.  Tiles that need
+  // no mask for any wave of the workgroup come first; the tail of the key
   // range and the diagonal tiles follow with the masked path.
   int n_plain = min(n_tiles, n_full);
   if (CAUSAL) n_plain = min(n_plain, (q0 + 1) / S::kBC);
   int t = 0;
   for (; t < n_plain; ++t) {
-    if (t + 1 < n_tiles) load_tile(t + 1);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     __syncthreads();
+    if (t + 1 < n_tiles) issue_tile(t + 1);
     process(std::false_type{}, t & 1, t * S::kBC);
-    if (t + 1 < n_tiles) store_tile((t + 1) & 1);
   }
   for (; t < n_tiles; ++t) {
-    if (t + 1 < n_tiles) load_tile(t + 1);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     __syncthreads();
+    if (t + 1 < n_tiles) issue_tile(t + 1);
     const int kv0 = t * S::kBC;
     if (!CAUSAL || kv0 <= wave_last_row) process(std::true_type{}, t & 1, kv0);
-    if (t + 1 < n_tiles) store_tile((t + 1) & 1);
   }
 
   // ---- epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2 ----
