@@ -71,7 +71,8 @@ typedef enum {
   ATTN_ERR_LAYOUT = 4,      /* misaligned base pointer, stride not a multiple of
                                16 bytes, or negative stride */
   ATTN_ERR_UNSUPPORTED = 5, /* valid arguments with no kernel (head_dim, dtype or
-                               group size outside the supported set) */
+                               group size outside the supported set, sizes past
+                               the documented limits) */
   ATTN_ERR_WORKSPACE = 6,   /* decode workspace NULL or smaller than required */
   ATTN_ERR_HIP = 7          /* the HIP runtime refused the launch */
 } attn_status_t;
@@ -116,9 +117,11 @@ typedef struct {
 /*
  * attn_fwd - prefill attention forward, one kernel launch.
  * Supported: dtype bf16 or f32; d in {64, 80, 128}; Hq % Hkv == 0; causal
- * needs Lq == Lk.  Any size may be 0: then nothing is launched (Lk == 0 with
- * Lq > 0 writes O = 0 and LSE = -inf).  Returns ATTN_OK or the first error
- * found; on error nothing is enqueued.
+ * needs Lq == Lk.  Limits (ATTN_ERR_UNSUPPORTED past them): Lq, Lk and
+ * B * Hq below 2^31; bf16 K and V token strides below 2^28 elements.  Any
+ * size may be 0: then nothing is launched (Lk == 0 with Lq > 0 writes O = 0
+ * and LSE = -inf).  Returns ATTN_OK or the first error found; on error
+ * nothing is enqueued.
  */
 attn_status_t attn_fwd(const attn_fwd_args_t *args, void *stream);
 

@@ -65,6 +65,9 @@ extern "C" attn_status_t attn_validate_fwd(const attn_fwd_args_t* a) {
     return ATTN_ERR_LAYOUT;
   // Index ranges the kernels keep in 32 bits, and the grid limits.
   if (a->Lq > kI32Max || a->Lk > kI32Max || a->B * a->Hq > kI32Max) return ATTN_ERR_UNSUPPORTED;
+  if (a->dtype == ATTN_BF16 && a->Lk > 0 &&
+      (a->k_strides[2] >= attn_dev::kFwdMaxTokenStride || a->v_strides[2] >= attn_dev::kFwdMaxTokenStride))
+    return ATTN_ERR_UNSUPPORTED;
   if ((a->Lq + 127) / 128 > kGridYMax || a->B * a->Hq * ((a->Lq + 127) / 128) > kI32Max)
     return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
@@ -102,7 +105,7 @@ static attn_status_t launch_fwd_bf16(const FwdParams& p, int grid_x, hipStream_t
   }
   FwdParams q = p;
   q.n_qtiles = (p.Lq + Bf16FwdShape<D>::kBR - 1) / Bf16FwdShape<D>::kBR;
-  hipLaunchKernelGGL(kern, dim3(grid_x * q.n_qtiles), dim3(256), lds, s, q);
+  hipLaunchKernelGGL(kern, dim3(grid_x * q.n_qtiles), dim3(64 * Bf16FwdShape<D>::kWaves), lds, s, q);
   return launch_status();
 }
 

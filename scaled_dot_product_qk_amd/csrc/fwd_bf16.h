@@ -96,6 +96,7 @@ __host__ __device__ constexpr int bf16_fwd_rows_per_workgroup(int d) {
 template <int D>
 struct Bf16FwdShape {
   static constexpr int kWaves = 4;
+  static constexpr int kGroupsPerCU = 8 / kWaves;  // workgroups resident per CU (2 waves per SIMD)
   static constexpr int kNB = bf16_fwd_blocks_per_wave(D);
   static constexpr int kRowsPerWave = 32 * kNB;
   static constexpr int kBR = kRowsPerWave * kWaves;  // query rows per workgroup
@@ -115,7 +116,7 @@ struct Bf16FwdShape {
   static constexpr int kKVar = kPitch == 8 ? 2 : 4;  // K swizzle patterns across one wave's copies
   static_assert(D % 16 == 0, "head_dim must be a multiple of 16");
   static_assert(kChunks <= kPitch && 2 * kDP <= kRowBytes, "a padded row must fit its LDS pitch");
-  static_assert(kCopiesPerWave % kKVar == 0 && 2 * kCopiesPerWave * kRowsPerCopy == kBC,
+  static_assert(kCopiesPerWave % kKVar == 0 && (kWaves / 2) * kCopiesPerWave * kRowsPerCopy == kBC,
                 "each wave copies whole swizzle periods of one of the two tiles");
   static_assert(kBufBytes < 65536, "in-buffer LDS offsets must fit the instruction offset field");
 };
@@ -138,14 +139,19 @@ __device__ __forceinline__ int fwd_v_swz(int r) {
   return (PITCH / 4) * (r & 3);
 }
 
-// 16 bytes per lane from global memory into LDS at lds_base + 16 * lane
-// (lds_base wave-uniform).  Inline assembly, so that the compiler neither
-// counts the copy among its outstanding loads nor makes LDS reads and barriers
-// wait for it: the kernel waits for its copies itself (vmcnt) before the
-// barrier that publishes them.
-__device__ __forceinline__ void fwd_copy16(const void* src, uint32_t lds_base) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_base) : "memory");
+// 16 bytes per lane from global memory at base + off (base wave-uniform, off
+// a per-lane byte offset) into LDS at lds_base + 16 * lane (lds_base
+// wave-uniform).  Inline assembly, so that the compiler neither counts the
+// copy among its outstanding loads nor makes LDS reads and barriers wait for
+// it: the kernel waits for its copies itself (vmcnt) before the barrier that
+// publishes them.
+__device__ __forceinline__ void fwd_copy16(const void* base, uint32_t off, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_base) : "memory");
 }
+
+// Largest K/V token stride (elements) the copies' 32-bit lane offsets allow:
+// a lane's offset spans at most 7 rows plus one row's chunks.
+constexpr int64_t kFwdMaxTokenStride = int64_t(1) << 28;
 
 // Row maxima are tracked in the log2 domain of the scaled scores, as a
 // reference m that only moves when it must.  Each tile's probabilities are
@@ -160,7 +166,8 @@ constexpr float kSumGuard = 256.f;
 static_assert(kSumGuard == float(1 << int(kRescaleLog2)), "guard is 2^kRescaleLog2");
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams p) {
+__global__ __launch_bounds__(64 * Bf16FwdShape<D>::kWaves, Bf16FwdShape<D>::kGroupsPerCU) void
+attn_fwd_bf16_kernel(FwdParams p) {
   using S = Bf16FwdShape<D>;
   constexpr int NB = S::kNB;
   typedef __attribute__((address_space(3))) char lds_char;
@@ -225,16 +232,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams p) {
   const int cp_row = lane / S::kPitch;  // row within one copy
   const int cp_row0 = S::kRowsPerCopy * ((wave % (S::kWaves / 2)) * S::kCopiesPerWave);
   const uint32_t cp_lds0 = (uint32_t)(uintptr_t)lds_b + (copies_k ? 0 : S::kTileBytes) + cp_row0 * S::kRowBytes;
-  int cp_chunk8[S::kKVar];   // 8 x logical chunk
-  int64_t cp_off[S::kKVar];  // element offset of the lane's chunk within its copy
+  int cp_chunk16[S::kKVar];   // byte offset of the lane's logical chunk
+  uint32_t cp_off[S::kKVar];  // byte offset of the lane's chunk within its copy
   bool cp_on[S::kKVar];
+  const uint32_t cp_row_bytes = (uint32_t)(2 * cp_st);  // < 2^29: token strides are validated
 #pragma unroll
   for (int v = 0; v < S::kKVar; ++v) {
     const int r = S::kRowsPerCopy * v + cp_row;  // row index modulo the swizzle period
     const int pc = lane % S::kPitch;
     const int lc = pc ^ (copies_k ? fwd_k_swz<S::kPitch>(r) : fwd_v_swz<S::kPitch>(r));
-    cp_chunk8[v] = 8 * lc;
-    cp_off[v] = (int64_t)cp_row * cp_st + 8 * lc;
+    cp_chunk16[v] = 16 * lc;
+    cp_off[v] = (uint32_t)cp_row * cp_row_bytes + 16 * lc;
     cp_on[v] = lc < S::kChunks;
   }
   // Full tiles copy without checks; the tile holding key Lk - 1 reads rows
@@ -248,15 +256,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams p) {
       for (int j = 0; j < S::kCopiesPerWave; ++j) {
         const uint16_t* src = cp_src + (int64_t)(kv0 + cp_row0 + S::kRowsPerCopy * j) * cp_st;
         if (S::kChunks == S::kPitch || cp_on[j % S::kKVar])
-          fwd_copy16(src + cp_off[j % S::kKVar], dst + j * S::kRowsPerCopy * S::kRowBytes);
+          fwd_copy16(src, cp_off[j % S::kKVar], dst + j * S::kRowsPerCopy * S::kRowBytes);
       }
     } else {
       const int last = p.Lk - 1;
 #pragma unroll
       for (int j = 0; j < S::kCopiesPerWave; ++j) {
-        const int key = min(kv0 + cp_row0 + S::kRowsPerCopy * j + cp_row, last);
+        const int row0 = min(kv0 + cp_row0 + S::kRowsPerCopy * j, last);
+        const int row = min(kv0 + cp_row0 + S::kRowsPerCopy * j + cp_row, last);
         if (S::kChunks == S::kPitch || cp_on[j % S::kKVar])
-          fwd_copy16(cp_src + (int64_t)key * cp_st + cp_chunk8[j % S::kKVar],
+          fwd_copy16(cp_src + (int64_t)row0 * cp_st, (uint32_t)(row - row0) * cp_row_bytes + cp_chunk16[j % S::kKVar],
                      dst + j * S::kRowsPerCopy * S::kRowBytes);
       }
     }
@@ -309,19 +318,36 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams p) {
   // which is possible because the probabilities of a half depend only on its
   // own scores and the reference max (see kSumGuard): each half has its own
   // guard, and a rescale of O after the first half's products is exact.
-  auto process = [&](auto mask_tag, int buf, int kv0) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  // tile_front runs all but the last products; the K operands of the first
+  // half come from ka_next, read ahead while the previous tile's last
+  // products ran (tile_back).
+  u32x4 ka_next[S::kKC];     // K operands, first key half of the next tile
+  u32x4 va_last[S::kND][2];  // V^T operands, second key half of this tile
+  u32x4 pop[NB][4];          // P^T B operands, one per 16-key slice
+  auto read_k = [&](int buf, int sb, u32x4 (&ka)[S::kKC]) {
     const lds_char* kb = lds_b + buf * S::kBufBytes;
+#pragma unroll
+    for (int kc = 0; kc < S::kKC; ++kc)
+      ka[kc] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+          kb + (k_rd ^ (32 * kc)) + 32 * sb * S::kRowBytes);
+  };
+  auto pv = [&](int sb, const u32x4 (&va)[S::kND][2]) {
+#pragma unroll
+    for (int db = 0; db < S::kND; ++db)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) oacc[nb][db] = mfma32(va[db][j], pop[nb][2 * sb + j], oacc[nb][db]);
+  };
+  auto tile_back = [&] {
+    __builtin_amdgcn_s_setprio(2);
+    pv(1, va_last);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto tile_front = [&](auto mask_tag, int buf, int kv0) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     lds_char* vb = lds_b + buf * S::kBufBytes;
     f32x16 s[NB][2];
-    u32x4 pop[NB][4];  // P^T B operands, one per 16-key slice
-
-    auto read_k = [&](int sb, u32x4 (&ka)[S::kKC]) {
-#pragma unroll
-      for (int kc = 0; kc < S::kKC; ++kc)
-        ka[kc] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-            kb + (k_rd ^ (32 * kc)) + 32 * sb * S::kRowBytes);
-    };
     auto read_v = [&](int sb, u32x4 (&va)[S::kND][2]) {
 #pragma unroll
       for (int db = 0; db < S::kND; ++db)
@@ -344,14 +370,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams p) {
       for (int kc = 0; kc < S::kKC; ++kc)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) s[nb][sb] = mfma32(ka[kc], qop[nb][kc], s[nb][sb]);
-    };
-    auto pv = [&](int sb, const u32x4 (&va)[S::kND][2]) {
-#pragma unroll
-      for (int db = 0; db < S::kND; ++db)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) oacc[nb][db] = mfma32(va[db][j], pop[nb][2 * sb + j], oacc[nb][db]);
     };
     // P = exp2(c s - m) for half sb of row block nb, packed as two P^T B
     // operands; returns this lane's share of the half's row sum.
@@ -424,49 +442,55 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams p) {
     };
 
     constexpr int kQKMfma = S::kKC * NB, kPVMfma = S::kND * 2 * NB;
-    u32x4 ka0[S::kKC], ka1[S::kKC], va0[S::kND][2], va1[S::kND][2];
-    read_k(0, ka0);
-    read_k(1, ka1);
+    u32x4 ka1[S::kKC], va0[S::kND][2];
+    read_k(buf, 1, ka1);
     __builtin_amdgcn_s_setprio(2);
-    qk(0, ka0);
+    qk(0, ka_next);
     __builtin_amdgcn_s_setprio(0);
     read_v(0, va0);
     qk(1, ka1);
     softmax_half(0, std::integral_constant<int, kQKMfma>{});
-    read_v(1, va1);
+    read_v(1, va_last);
     pv(0, va0);
     softmax_half(1, std::integral_constant<int, kPVMfma>{});
-    __builtin_amdgcn_s_setprio(2);
-    pv(1, va1);
-    __builtin_amdgcn_s_setprio(0);
   };
 
   // Q must have landed before the first copy: the copies are invisible to the
   // compiler, and a later wait for Q would not know to let them run on.
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   if (n_tiles > 0) issue_tile(0);
+  if (n_tiles > 1) {
+    issue_tile(1);
+    __builtin_amdgcn_s_waitcnt(0x0f70 | S::kCopiesPerWave);  // vmcnt: tile 0's copies done
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  }
+  __syncthreads();
+  auto active = [&](int t) { return !CAUSAL || t * S::kBC <= wave_last_row; };
+  if (n_tiles > 0 && active(0)) read_k(0, 0, ka_next);
 
-  // Iteration t: wait for this wave's copies of tile t, barrier (all copies
-  // of t are in LDS, and every wave is done with tile t - 1, whose buffer the
-  // copies of t + 1 then overwrite), copy t + 1, process t.  Tiles that need
-  // no mask for any wave of the workgroup come first; the tail of the key
-  // range and the diagonal tiles follow with the masked path.
+  // Step t: the front of tile t; then wait for this wave's copies of tile
+  // t + 1 and barrier (all copies of t + 1 are in LDS, every wave has read
+  // all it needs of tile t), copy tile t + 2 into tile t's buffer, read the
+  // first K operands of tile t + 1, and issue tile t's last products.  Tiles
+  // that need no mask for any wave of the workgroup come first; the tail of
+  // the key range and the diagonal tiles follow with the masked path.
+  auto step = [&](auto mask_tag, int t) {
+    const bool act = active(t);
+    if (act) tile_front(mask_tag, t & 1, t * S::kBC);
+    if (t + 1 < n_tiles) {
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+      __syncthreads();
+      if (t + 2 < n_tiles) issue_tile(t + 2);
+      if (active(t + 1)) read_k((t + 1) & 1, 0, ka_next);
+    }
+    if (act) tile_back();
+  };
   int n_plain = min(n_tiles, n_full);
   if (CAUSAL) n_plain = min(n_plain, (q0 + 1) / S::kBC);
   int t = 0;
-  for (; t < n_plain; ++t) {
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-    __syncthreads();
-    if (t + 1 < n_tiles) issue_tile(t + 1);
-    process(std::false_type{}, t & 1, t * S::kBC);
-  }
-  for (; t < n_tiles; ++t) {
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-    __syncthreads();
-    if (t + 1 < n_tiles) issue_tile(t + 1);
-    const int kv0 = t * S::kBC;
-    if (!CAUSAL || kv0 <= wave_last_row) process(std::true_type{}, t & 1, kv0);
-  }
+  for (; t < n_plain; ++t) step(std::false_type{}, t);
+  for (; t < n_tiles; ++t) step(std::true_type{}, t);
 
   // ---- epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2 ----
 #pragma unroll

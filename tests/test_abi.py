@@ -89,11 +89,19 @@ def test_fwd_valid_configurations(d, dtype, causal):
     (dict(ks=(-1, 300 * 64, 64)), LAYOUT),
     (dict(dtype=1, qs=(8 * 300 * 64, 300 * 64, 66)), LAYOUT),
     (dict(Lq=2 ** 31, Lk=2 ** 31), UNSUP),
+    (dict(ks=(8 * 300 * 64, 300 * 64, 2 ** 28)), UNSUP),   # K token stride past the copy limit
+    (dict(vs=(8 * 300 * 64, 300 * 64, 2 ** 28)), UNSUP),
 ])
 def test_fwd_rejections(kw, status):
     assert vfwd(**kw) == status
     assert run_fwd(**kw) == status
     assert sdpa.lib().attn_kernel_name(ctypes.byref(fwd_args(**kw))).decode() == "none"
+
+
+def test_fwd_token_stride_limit_is_bf16_only():
+    big = (8 * 300 * 64, 300 * 64, 2 ** 28 - 8)
+    assert vfwd(ks=big, vs=big) == OK
+    assert vfwd(dtype=1, ks=(8 * 300 * 64, 300 * 64, 2 ** 28), vs=(8 * 300 * 64, 300 * 64, 2 ** 28)) == OK
 
 
 def test_fwd_empty_inputs_are_valid_noops():
