@@ -36,10 +36,15 @@ KERNEL_SOURCES = [os.path.join(ROOT, "scaled_dot_product_qk_amd", "csrc", f)
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and blank space removed, so
+    that counters stay attached to a build whose code has not changed."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -8,8 +8,9 @@
 // (returned as LSE = m + ln l, section 五) are written.
 //
 // Work decomposition: one workgroup of 4 waves per (batch, query head, tile
-// of 128 query rows); wave w owns 32 rows.  Key/value tiles of 64 keys are
-// staged in LDS, double buffered, and shared by the 4 waves.
+// of query rows); wave w owns 64 rows at head_dim 64 and 32 rows otherwise.
+// Key/value tiles of 64 keys are copied from global memory straight into LDS,
+// double buffered, and shared by the 4 waves.
 //
 // Orientation: every product is taken transposed, S^T = K Q^T and
 // O^T = V^T P^T, so that in both the score accumulator and the output
@@ -19,15 +20,14 @@
 //   * the probabilities leave the score accumulator already in the B-operand
 //     layout of the P V product (no LDS round trip);
 //   * the rescale of the output by exp(m_old - m_new) is a per-lane scalar.
-// The key order inside each 16-key slice of the P V contraction is permuted to
-// match the score accumulator's row order; V^T is written to LDS in that
-// permuted order so each lane's 8 keys are one 16-byte read.
+// V stays row-major in LDS; the V^T operands come from the transposing LDS
+// read, visiting the keys of each 16-key slice in the score accumulator's row
+// order.
 //
 // Causal (top-left, Lq == Lk): key tiles entirely above a wave's last row are
 // skipped; tiles that straddle the diagonal or the end of the keys are masked
-// to -inf before the max.  Key tile 0 is processed first and always holds a
-// visible key for every row, so the running max is finite from the first tile
-// on and exp(-inf - m) = 0 never meets exp(-inf - (-inf)).
+// to -inf.  Key tile 0 is processed first and holds a visible key for every
+// row, so the reference max is finite after each row's first tile.
 #pragma once
 
 #include <type_traits>
