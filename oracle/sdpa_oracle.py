@@ -22,7 +22,12 @@ pages give it:
 
 Readings where the pages leave a step open (each also listed in the design
 notes):
-  * causal means top-left alignment with Lq == Lk: query i sees keys j <= i;
+  * causal means top-left alignment: query i sees keys j <= i, for any Lq
+    and Lk (the convention of the scaled_dot_product_attention call the pages
+    use; they do not say where the diagonal sits when Lq != Lk);
+  * packed variable-length batches (cnblogs FAQ Q10): sequence b owns query
+    rows cu_q[b] .. cu_q[b+1]-1 and key rows cu_k[b] .. cu_k[b+1]-1 and
+    attends only to its own keys, each sequence exactly as a batch of one;
   * a grouped-query head h reads key/value head h // (Hq / Hkv);
   * decode is one query token per sequence that sees cache slots 0..L_b-1;
     a length above the cache size is clamped to it;
@@ -135,8 +140,6 @@ def attention_forward(q, k, v, causal: bool = False, scale: Optional[float] = No
         raise ValueError("q, k, v shapes disagree")
     if Hkv == 0 or Hq % Hkv != 0:
         raise ValueError("query heads must be a multiple of key/value heads")
-    if causal and Lq != Lk:
-        raise ValueError("causal attention is defined here for Lq == Lk only")
     if scale is None:
         scale = default_scale(d)
     group = Hq // Hkv
@@ -162,6 +165,41 @@ def attention_forward(q, k, v, causal: bool = False, scale: Optional[float] = No
     return o, lse
 
 
+def attention_forward_varlen(q, k, v, cu_q: Sequence[int], cu_k: Sequence[int], causal: bool = False,
+                             scale: Optional[float] = None, threads: Optional[int] = None):
+    """Packed variable-length prefill (cnblogs FAQ Q10, cross-attention FAQ Q15).
+
+    q [total_q, Hq, d]; k, v [total_k, Hkv, d]; cu_q, cu_k the B + 1 sequence
+    offsets.  Each sequence is attention_forward's computation on its own rows
+    and keys.  Returns O [total_q, Hq, d] and LSE [Hq, total_q].
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    total_q, Hq, d = q.shape
+    total_k, Hkv, dk = k.shape
+    cu_q = [int(x) for x in cu_q]
+    cu_k = [int(x) for x in cu_k]
+    if dk != d or v.shape[:2] != k.shape[:2] or len(cu_q) != len(cu_k):
+        raise ValueError("q, k, v or the offsets disagree")
+    if Hkv == 0 or Hq % Hkv != 0:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    if scale is None:
+        scale = default_scale(d)
+    group = Hq // Hkv
+    o = np.zeros((total_q, Hq, v.shape[2]))
+    lse = np.full((Hq, total_q), -np.inf)
+    items = [(b, h) for b in range(len(cu_q) - 1) for h in range(Hq)]
+
+    def one(item):
+        b, h = item
+        qs, qe, ks, ke = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        return _head_attention(q[qs:qe, h], k[ks:ke, h // group], v[ks:ke, h // group], scale, causal)
+
+    for (b, h), (ob, lb) in zip(items, _pool_map(one, items, threads)):
+        o[cu_q[b]:cu_q[b + 1], h] = ob
+        lse[h, cu_q[b]:cu_q[b + 1]] = lb
+    return o, lse
+
+
 def attention_forward_rows(q, k, v, b: int, h: int, rows: Iterable[int],
                            causal: bool = False, scale: Optional[float] = None):
     """The same definition for a few query rows of one (batch, query head).
@@ -176,8 +214,6 @@ def attention_forward_rows(q, k, v, b: int, h: int, rows: Iterable[int],
     rows = np.asarray(list(rows), dtype=np.int64)
     if scale is None:
         scale = default_scale(q.shape[-1])
-    if causal and q.shape[2] != k.shape[2]:
-        raise ValueError("causal attention is defined here for Lq == Lk only")
     return _head_attention(q_bh[rows], _as64(k[b, hk]), _as64(v[b, hk]), scale,
                            causal, row_ids=rows)
 

@@ -299,6 +299,80 @@ def test_input_recipe_is_bf16_round_to_nearest_even():
     assert np.array_equal(rounded, got)
 
 
+# ------------------------------------- P-14 cross-attention, Lq != Lk
+@pytest.mark.parametrize("Lq,Lk", [(5, 9), (9, 5), (1, 7), (7, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_cross_attention_matches_brute_force(Lq, Lk, causal):
+    q, k, v = rnd((1, 2, Lq, 4), 70, 2.0), rnd((1, 2, Lk, 4), 71), rnd((1, 2, Lk, 4), 72)
+    o, lse = orc.attention_forward(q, k, v, causal=causal)
+    ob, lb = orc.brute_force_attention(q.tolist(), k.tolist(), v.tolist(), causal=causal)
+    assert np.abs(o - np.array(ob)).max() <= 1e-12
+    assert np.abs(lse - np.array(lb)).max() <= 1e-12
+
+
+@pytest.mark.parametrize("Lq,Lk", [(20, 33), (33, 20)])
+def test_cross_attention_causal_matches_torch_sdpa_float64(Lq, Lk):
+    # torch's is_causal is top-left (a lower-triangular L x S mask), the reading taken
+    q, k, v = rnd((2, 4, Lq, 16), 73, 2.0), rnd((2, 4, Lk, 16), 74), rnd((2, 4, Lk, 16), 75)
+    o, _ = orc.attention_forward(q, k, v, causal=True)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=True).numpy()
+    assert np.abs(o - ref).max() <= 1e-12
+
+
+def test_causal_rows_past_the_last_key_see_every_key():
+    # top-left with Lq > Lk: rows i >= Lk - 1 see all keys, i.e. equal the non-causal rows
+    q, k, v = rnd((1, 2, 30, 8), 76), rnd((1, 2, 12, 8), 77), rnd((1, 2, 12, 8), 78)
+    oc, lc = orc.attention_forward(q, k, v, causal=True)
+    on, ln = orc.attention_forward(q, k, v, causal=False)
+    assert np.array_equal(oc[:, :, 11:], on[:, :, 11:]) and np.array_equal(lc[:, :, 11:], ln[:, :, 11:])
+    assert np.abs(oc[:, :, :11] - on[:, :, :11]).max() > 1e-3
+
+
+# ------------------------------------------- P-15 packed variable length
+VARLEN_CASES = [  # (query lengths, key lengths)
+    ([3, 0, 5, 1], [4, 2, 5, 3]),   # an empty sequence
+    ([2, 4], [0, 6]),               # a sequence with queries but no keys
+    ([6], [6]),
+    ([4, 7, 2], [7, 4, 2]),         # Lq != Lk per sequence
+]
+
+
+@pytest.mark.parametrize("case", range(len(VARLEN_CASES)))
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_matches_brute_force_per_sequence(case, causal):
+    lq, lk = VARLEN_CASES[case]
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    Hq, Hkv, d = 4, 2, 4
+    q = rnd((cu_q[-1], Hq, d), 80 + case, 2.0)
+    k, v = rnd((cu_k[-1], Hkv, d), 90 + case), rnd((cu_k[-1], Hkv, d), 100 + case)
+    o, lse = orc.attention_forward_varlen(q, k, v, cu_q, cu_k, causal=causal)
+    for b in range(len(lq)):
+        qs, qe, ks, ke = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        if qe == qs:
+            continue
+        qb = q[qs:qe].transpose(1, 0, 2)[None]   # [1, Hq, Lq_b, d]
+        kb = k[ks:ke].transpose(1, 0, 2)[None]
+        vb = v[ks:ke].transpose(1, 0, 2)[None]
+        ob, lb = orc.brute_force_attention(qb.tolist(), kb.tolist(), vb.tolist(), causal=causal)
+        ob = np.array(ob)[0].transpose(1, 0, 2) if ke > ks else np.zeros((qe - qs, Hq, d))
+        assert np.abs(o[qs:qe] - ob).max() <= 1e-12
+        assert np.array_equal(np.isneginf(lse[:, qs:qe]), np.isneginf(np.array(lb)[0]))
+        fin = np.isfinite(np.array(lb)[0])
+        assert np.abs(lse[:, qs:qe][fin] - np.array(lb)[0][fin]).max(initial=0.0) <= 1e-12
+    if 0 in lk:  # rows of a sequence without keys
+        b = lk.index(0)
+        assert (o[cu_q[b]:cu_q[b + 1]] == 0).all() and np.isneginf(lse[:, cu_q[b]:cu_q[b + 1]]).all()
+
+
+def test_varlen_single_sequence_is_dense():
+    q, k, v = rnd((1, 4, 9, 8), 110), rnd((1, 2, 11, 8), 111), rnd((1, 2, 11, 8), 112)
+    o, lse = orc.attention_forward(q, k, v, causal=True)
+    ov, lv = orc.attention_forward_varlen(q[0].transpose(1, 0, 2), k[0].transpose(1, 0, 2),
+                                          v[0].transpose(1, 0, 2), [0, 9], [0, 11], causal=True)
+    assert np.array_equal(ov, o[0].transpose(1, 0, 2)) and np.array_equal(lv, lse[0])
+
+
 # -------------------------------------------- planted mistakes are caught
 def _mutant(kind):
     """Copies of the oracle's per-head step with one plausible slip each."""
@@ -333,7 +407,9 @@ def test_planted_mistakes(monkeypatch, kind):
     for fn in (lambda: test_matches_torch_sdpa_float64(True, 4, 4),
                lambda: test_causal_first_row_is_first_value(),
                lambda: test_key_shift_moves_only_lse(True),
-               lambda: test_constant_values_return_the_constant(False)):
+               lambda: test_constant_values_return_the_constant(False),
+               lambda: test_cross_attention_causal_matches_torch_sdpa_float64(20, 33),
+               lambda: test_varlen_matches_brute_force_per_sequence(3, True)):
         try:
             fn()
         except AssertionError:
