@@ -6,6 +6,9 @@ One step = one pass of the whole path over synthetic, HBM-resident inputs:
   3. attn_decode, B=64, Hq=32, Hkv=8, d=128, cache lengths U{1024..8192}, bf16
 Each call is timed with HIP events recorded on the stream the kernels run on;
 the step as a whole is timed with host clocks between device synchronisations.
+After the step loop, attn_fwd_varlen on 16 packed causal GQA sequences of
+256..4096 tokens (d=128) is timed the same way on its own and reported in
+`extra` (it is not part of the step).
 
 Prints ONE JSON line.  `value` is the headline workload's attention-forward
 throughput in TFLOP/s (credited flops 4 n^2 d H B, halved when causal).
@@ -68,7 +71,8 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "fwd_n4096", "fwd_causal_n8192", "decode"], default="all",
+    ap.add_argument("--only", choices=["all", "fwd_n4096", "fwd_causal_n8192", "decode", "fwd_varlen"],
+                    default="all",
                     help="time one call of the step only (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=96)
@@ -121,7 +125,9 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
 
-    names = ["fwd_n4096", "fwd_causal_n8192", "decode"] if args.only == "all" else [args.only]
+    names = ["fwd_n4096", "fwd_causal_n8192", "decode"] if args.only == "all" else \
+        ([] if args.only == "fwd_varlen" else [args.only])
+    with_varlen = args.only in ("all", "fwd_varlen")
 
     # ---- inputs, generated on the host and copied once to HBM ----
     calls = {}
@@ -147,10 +153,18 @@ def main():
         ws = torch.empty(sdpa.attn_decode_workspace_bytes(wl.C5.B, wl.C5.Hq, wl.C5.Lmax, wl.C5.d),
                          dtype=torch.uint8, device=dev)
         calls["decode"] = lambda: sdpa.attn_decode(*GD, workspace=ws, out=od, lse=ld, stream=stream)
+    if with_varlen:
+        qv, kv_, vv, cqv, ckv = wl.make_varlen_inputs(wl.C6)
+        GV = [t.to(dev) for t in (qv, kv_, vv, cqv, ckv)]
+        lens_v = (cqv[1:] - cqv[:-1]).tolist()
+        ov = torch.empty_like(GV[0])
+        lv = torch.empty((wl.C6.Hq, GV[0].shape[0]), dtype=torch.float32, device=dev)
+        calls["fwd_varlen"] = lambda: sdpa.attn_fwd_varlen(*GV, max(lens_v), causal=True, out=ov, lse=lv,
+                                                           stream=stream)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
-        for n in names:
+        for n in names + (["fwd_varlen"] if with_varlen else []):
             calls[n]()
     torch.cuda.synchronize()
 
@@ -167,7 +181,17 @@ def main():
             ev[n].append((a, b))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / len(ev[n]) for n in names}
+    if with_varlen:  # timed on its own, outside the step
+        ev["fwd_varlen"] = []
+        for _ in range(args.steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            calls["fwd_varlen"]()
+            b.record(stream)
+            ev["fwd_varlen"].append((a, b))
+        torch.cuda.synchronize()
+    ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / len(ev[n]) for n in ev}
 
     # ---- accounting ----
     C2, C4, C5 = wl.C2, wl.C4, wl.C5
@@ -189,6 +213,14 @@ def main():
         res["decode"] = {"kernel": "attn_decode_split_kernel<128> + attn_decode_merge_kernel<128>",
                          "ms": ms["decode"], "gbps": bd / t / 1e9, "algorithmic_bytes": bd,
                          "total_cache_keys": int(lens.sum())}
+
+    if "fwd_varlen" in ms:
+        C6 = wl.C6
+        t = ms["fwd_varlen"] / 1e3
+        fv = wl.algorithmic_flops_varlen(lens_v, lens_v, C6.Hq, C6.d, C6.causal)
+        res["fwd_varlen"] = {"kernel": "attn_fwd_bf16_d128_causal (packed sequences)", "ms": ms["fwd_varlen"],
+                             "tflops": fv / t / 1e12, "algorithmic_flops": fv,
+                             "total_tokens": int(sum(lens_v)), "sequences": C6.B}
 
     def roof_fwd(r, tag):
         tr = counted_traffic(tag)
@@ -222,6 +254,9 @@ def main():
         out["extra"]["decode_b64_gqa_d128"] = dict(r, roofline={
             "bound": "hbm", "achieved": r["gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": r["gbps"] / PEAK_HBM_GBPS, "traffic": counted_traffic("attn_decode_d128_b64")})
+    if "fwd_varlen" in res:
+        r = res["fwd_varlen"]
+        out["extra"]["fwd_varlen_causal_gqa_b16_d128"] = dict(r, roofline=roof_fwd(r, "attn_fwd_varlen_d128_causal_b16"))
     if headline:
         out["extra"]["fwd_n4096_d64"] = headline
     if not args.no_cpu_baseline and args.only in ("all", "fwd_n4096"):

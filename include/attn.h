@@ -6,7 +6,7 @@
  * hk = h / (Hq / Hkv)):
  *
  *     S   = Q[b,h] K[b,hk]^T * scale           scores, one row per query
- *     S[i,j] = -inf where j > i                 only when causal
+ *     S[i,j] = -inf where j > i                 only when causal (top-left)
  *     P   = softmax(S) along the key axis       after subtracting the row max
  *     O   = P V[b,hk]
  *     LSE = m + ln(l) per row                   m = row max, l = sum exp(S - m)
@@ -66,7 +66,7 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
   ATTN_ERR_SHAPE = 2,       /* negative size, Hkv == 0 with work to do, Hq % Hkv != 0,
-                               causal with Lq != Lk */
+                               max_seqlen_q > total_q, non-finite scale */
   ATTN_ERR_DTYPE = 3,       /* dtype not one of attn_dtype_t */
   ATTN_ERR_LAYOUT = 4,      /* misaligned base pointer, stride not a multiple of
                                16 bytes, or negative stride */
@@ -91,9 +91,35 @@ typedef struct {
   int64_t v_strides[3];
   int64_t o_strides[3];
   int32_t dtype;   /* attn_dtype_t */
-  int32_t causal;  /* nonzero: query i sees keys j <= i (top-left; needs Lq == Lk) */
+  int32_t causal;  /* nonzero: query i sees keys j <= i (top-left, any Lq and Lk) */
   float scale;     /* multiplier of Q K^T; 0 selects 1/sqrt(d) */
 } attn_fwd_args_t;
+
+/* Packed variable-length prefill ("Flash Attention原理：分块计算与重计算"
+ * (cnblogs), FAQ Q10: several sequences of different lengths packed into one
+ * batch through cumulative sequence offsets, no padding; FAQ Q15: queries and
+ * keys/values of different lengths, as in cross-attention).  Sequence b owns
+ * query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key/value rows
+ * cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1; it attends only to its own keys. */
+typedef struct {
+  const void *q;   /* [total_q, Hq,  d] */
+  const void *k;   /* [total_k, Hkv, d] */
+  const void *v;   /* [total_k, Hkv, d] */
+  void *o;         /* [total_q, Hq,  d], same dtype as q */
+  float *lse;      /* [Hq, total_q] fp32, contiguous */
+  const int32_t *cu_seqlens_q;  /* device, B + 1 entries: 0, ..., total_q, non-decreasing */
+  const int32_t *cu_seqlens_k;  /* device, B + 1 entries: 0, ..., total_k, non-decreasing */
+  int64_t B, Hq, Hkv, total_q, total_k;
+  int64_t max_seqlen_q;  /* >= every query length (host-side: sizes the grid) */
+  int64_t d;
+  int64_t q_strides[2];  /* element strides of (token, head); d stride is 1 */
+  int64_t k_strides[2];
+  int64_t v_strides[2];
+  int64_t o_strides[2];
+  int32_t dtype;   /* attn_dtype_t; ATTN_BF16 */
+  int32_t causal;  /* nonzero: within each sequence, query i sees keys j <= i */
+  float scale;     /* multiplier of Q K^T; 0 selects 1/sqrt(d) */
+} attn_fwd_varlen_args_t;
 
 /* Decode: one query token per sequence against a ragged KV cache. */
 typedef struct {
@@ -116,14 +142,30 @@ typedef struct {
 
 /*
  * attn_fwd - prefill attention forward, one kernel launch.
- * Supported: dtype bf16 or f32; d in {64, 80, 128}; Hq % Hkv == 0; causal
- * needs Lq == Lk.  Limits (ATTN_ERR_UNSUPPORTED past them): Lq, Lk and
- * B * Hq below 2^31; bf16 K and V token strides below 2^28 elements.  Any
- * size may be 0: then nothing is launched (Lk == 0 with Lq > 0 writes O = 0
- * and LSE = -inf).  Returns ATTN_OK or the first error found; on error
- * nothing is enqueued.
+ * Supported: dtype bf16 or f32; d in {64, 80, 128}; Hq % Hkv == 0; Lq and
+ * Lk independent (cross-attention), causal or not.  Limits
+ * (ATTN_ERR_UNSUPPORTED past them): Lq, Lk and B * Hq below 2^31; bf16 K and
+ * V token strides below 2^28 elements.  Any size may be 0: then nothing is
+ * launched (rows that see no key -- Lk == 0 -- get O = 0 and LSE = -inf).
+ * Returns ATTN_OK or the first error found; on error nothing is enqueued.
  */
 attn_status_t attn_fwd(const attn_fwd_args_t *args, void *stream);
+
+/*
+ * attn_fwd_varlen - packed variable-length prefill, one kernel launch: the
+ * same computation as attn_fwd applied to each sequence separately.
+ * Supported: dtype bf16; d in {64, 80, 128}; Hq % Hkv == 0;
+ * 0 <= max_seqlen_q <= total_q.  Limits as attn_fwd (total_q, total_k below
+ * 2^31; K/V token strides below 2^28 elements).  The offsets live in device
+ * memory and are not checked on the host: the caller guarantees the form
+ * above and max_seqlen_q >= every query length (a longer sequence's rows
+ * past max_seqlen_q, rounded up to the kernel's query tile, are not written).
+ * Offsets outside [0, total] are
+ * clamped on the device, so inconsistent offsets give wrong rows, never an
+ * access outside the tensors.  Sequences with no keys get O = 0 and
+ * LSE = -inf.  B == 0, Hq == 0 or max_seqlen_q == 0 is a no-op.
+ */
+attn_status_t attn_fwd_varlen(const attn_fwd_varlen_args_t *args, void *stream);
 
 /*
  * attn_decode_workspace_bytes - bytes of device workspace attn_decode needs
@@ -151,6 +193,7 @@ attn_status_t attn_decode(const attn_decode_args_t *args, void *workspace,
 /* Argument checks only (no device work, no HIP call): the status attn_fwd /
  * attn_decode would return before launching.  Usable without a GPU. */
 attn_status_t attn_validate_fwd(const attn_fwd_args_t *args);
+attn_status_t attn_validate_fwd_varlen(const attn_fwd_varlen_args_t *args);
 attn_status_t attn_validate_decode(const attn_decode_args_t *args);
 
 /* Static, human-readable name of a status code. */

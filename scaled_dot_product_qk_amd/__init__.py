@@ -20,8 +20,9 @@ ATTN_BF16, ATTN_F32 = 0, 1
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_DTYPE",
                 4: "ATTN_ERR_LAYOUT", 5: "ATTN_ERR_UNSUPPORTED", 6: "ATTN_ERR_WORKSPACE",
                 7: "ATTN_ERR_HIP"}
-EXPORTED = ("attn_fwd", "attn_decode", "attn_decode_workspace_bytes", "attn_validate_fwd",
-            "attn_validate_decode", "attn_status_str", "attn_kernel_name", "attn_version")
+EXPORTED = ("attn_fwd", "attn_fwd_varlen", "attn_decode", "attn_decode_workspace_bytes",
+            "attn_validate_fwd", "attn_validate_fwd_varlen", "attn_validate_decode", "attn_status_str",
+            "attn_kernel_name", "attn_version")
 
 _i64 = ctypes.c_int64
 _i64x3 = _i64 * 3
@@ -34,6 +35,17 @@ class FwdArgs(ctypes.Structure):
                 ("B", _i64), ("Hq", _i64), ("Hkv", _i64), ("Lq", _i64), ("Lk", _i64), ("d", _i64),
                 ("q_strides", _i64x3), ("k_strides", _i64x3), ("v_strides", _i64x3),
                 ("o_strides", _i64x3),
+                ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class FwdVarlenArgs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+                ("B", _i64), ("Hq", _i64), ("Hkv", _i64), ("total_q", _i64), ("total_k", _i64),
+                ("max_seqlen_q", _i64), ("d", _i64),
+                ("q_strides", _i64x2), ("k_strides", _i64x2), ("v_strides", _i64x2),
+                ("o_strides", _i64x2),
                 ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
@@ -67,6 +79,10 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd.restype = ctypes.c_int
         L.attn_validate_fwd.argtypes = [ctypes.POINTER(FwdArgs)]
         L.attn_validate_fwd.restype = ctypes.c_int
+        L.attn_fwd_varlen.argtypes = [ctypes.POINTER(FwdVarlenArgs), ctypes.c_void_p]
+        L.attn_fwd_varlen.restype = ctypes.c_int
+        L.attn_validate_fwd_varlen.argtypes = [ctypes.POINTER(FwdVarlenArgs)]
+        L.attn_validate_fwd_varlen.restype = ctypes.c_int
         L.attn_kernel_name.argtypes = [ctypes.POINTER(FwdArgs)]
         L.attn_kernel_name.restype = ctypes.c_char_p
         L.attn_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p, ctypes.c_size_t,
@@ -164,6 +180,63 @@ def attn_fwd(q, k, v, causal: bool = False, scale: Optional[float] = None, out=N
     st = lib().attn_fwd(ctypes.byref(args), _stream_handle(stream))
     if st != 0:
         raise AttnError(st, "attn_fwd")
+    return out, lse
+
+
+def make_fwd_varlen_args(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, o, lse, causal: bool,
+                         scale: Optional[float]) -> FwdVarlenArgs:
+    a = FwdVarlenArgs()
+    a.q, a.k, a.v, a.o, a.lse = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr()
+    a.cu_seqlens_q, a.cu_seqlens_k = cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr()
+    a.B = cu_seqlens_q.numel() - 1
+    a.total_q, a.Hq, a.d = q.shape
+    a.total_k, a.Hkv = k.shape[0], k.shape[1]
+    a.max_seqlen_q = int(max_seqlen_q)
+    a.q_strides = _i64x2(*q.stride()[:2])
+    a.k_strides = _i64x2(*k.stride()[:2])
+    a.v_strides = _i64x2(*v.stride()[:2])
+    a.o_strides = _i64x2(*o.stride()[:2])
+    a.dtype = _dtype_code(q)
+    a.causal = 1 if causal else 0
+    a.scale = 0.0 if scale is None else float(scale)
+    return a
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: bool = False,
+                    scale: Optional[float] = None, out=None, lse=None,
+                    stream=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """O [total_q,Hq,d] and LSE [Hq,total_q] of packed variable-length attention:
+    q [total_q,Hq,d], k/v [total_k,Hkv,d], int32 device offsets cu_seqlens_q/k
+    of B + 1 entries; max_seqlen_q (a host int) bounds every query length."""
+    import torch
+    _check_device(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or k.shape != v.shape or k.shape[2] != q.shape[2]:
+        raise ValueError(f"q must be [total_q,Hq,d], k and v [total_k,Hkv,d]; got "
+                         f"{tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    for t in (q, k, v):
+        if t.numel() and t.stride(2) != 1:
+            raise ValueError("head_dim must be the innermost, contiguous dimension")
+    for c in (cu_seqlens_q, cu_seqlens_k):
+        if c.dtype != torch.int32 or c.dim() != 1 or not c.is_contiguous():
+            raise ValueError("cu_seqlens must be contiguous 1-D int32 tensors")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k need the same B + 1 >= 1 entries")
+    total_q, Hq, d = q.shape
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    _check_device(q, out, lse)
+    if not lse.is_contiguous() or lse.dtype != torch.float32 or lse.shape != (Hq, total_q):
+        raise ValueError("lse must be a contiguous float32 [Hq, total_q] tensor")
+    if out.shape != q.shape or out.dtype != q.dtype or (out.numel() and out.stride(2) != 1):
+        raise ValueError("out must match q's shape and dtype with a contiguous head_dim")
+    args = make_fwd_varlen_args(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, out, lse, causal, scale)
+    st = lib().attn_fwd_varlen(ctypes.byref(args), _stream_handle(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_varlen")
     return out, lse
 
 

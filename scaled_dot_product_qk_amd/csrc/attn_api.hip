@@ -53,7 +53,6 @@ extern "C" attn_status_t attn_validate_fwd(const attn_fwd_args_t* a) {
   if (!fwd_head_dim_supported(a->d)) return ATTN_ERR_UNSUPPORTED;
   const bool work = a->B > 0 && a->Hq > 0 && a->Lq > 0;
   if (a->Hq > 0 && (a->Hkv == 0 || a->Hq % a->Hkv != 0)) return ATTN_ERR_SHAPE;
-  if (a->causal && a->Lq != a->Lk) return ATTN_ERR_SHAPE;
   if (!work) return ATTN_OK;
   if (!a->q || !a->o || !a->lse) return ATTN_ERR_NULL;
   if (a->Lk > 0 && (!a->k || !a->v)) return ATTN_ERR_NULL;
@@ -142,6 +141,11 @@ extern "C" attn_status_t attn_fwd(const attn_fwd_args_t* a, void* stream) {
   p.Lq = (int)a->Lq;
   p.Lk = (int)a->Lk;
   p.n_qtiles = (int)((a->Lq + 127) / 128);
+  p.lse_sb = a->Hq * a->Lq;
+  p.lse_sh = a->Lq;
+  p.cu_q = nullptr;
+  p.cu_k = nullptr;
+  p.total_q = p.total_k = 0;
   p.scale_log2 = effective_scale(a->scale, a->d) * kLog2e;
   p.scale_log2_abs = std::fabs(p.scale_log2);
   p.neg_q = p.scale_log2 < 0.f ? 1 : 0;
@@ -160,6 +164,74 @@ extern "C" attn_status_t attn_fwd(const attn_fwd_args_t* a, void* stream) {
       case 80: return c ? launch_fwd_f32<80, true>(p, grid_x, s) : launch_fwd_f32<80, false>(p, grid_x, s);
       case 128: return c ? launch_fwd_f32<128, true>(p, grid_x, s) : launch_fwd_f32<128, false>(p, grid_x, s);
     }
+  }
+  return ATTN_ERR_UNSUPPORTED;
+}
+
+extern "C" attn_status_t attn_validate_fwd_varlen(const attn_fwd_varlen_args_t* a) {
+  if (!a) return ATTN_ERR_NULL;
+  if (a->dtype != ATTN_BF16 && a->dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+  if (a->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (a->B < 0 || a->Hq < 0 || a->Hkv < 0 || a->total_q < 0 || a->total_k < 0 || a->max_seqlen_q < 0 ||
+      a->d < 0)
+    return ATTN_ERR_SHAPE;
+  if (a->max_seqlen_q > a->total_q) return ATTN_ERR_SHAPE;
+  if (!std::isfinite(a->scale)) return ATTN_ERR_SHAPE;
+  if (!fwd_head_dim_supported(a->d)) return ATTN_ERR_UNSUPPORTED;
+  if (a->Hq > 0 && (a->Hkv == 0 || a->Hq % a->Hkv != 0)) return ATTN_ERR_SHAPE;
+  const bool work = a->B > 0 && a->Hq > 0 && a->max_seqlen_q > 0;
+  if (!work) return ATTN_OK;
+  if (!a->q || !a->o || !a->lse || !a->cu_seqlens_q || !a->cu_seqlens_k) return ATTN_ERR_NULL;
+  if (a->total_k > 0 && (!a->k || !a->v)) return ATTN_ERR_NULL;
+  if (!aligned16(a->q) || !aligned16(a->o) || !aligned16(a->lse)) return ATTN_ERR_LAYOUT;
+  if (a->total_k > 0 && (!aligned16(a->k) || !aligned16(a->v))) return ATTN_ERR_LAYOUT;
+  if ((reinterpret_cast<uintptr_t>(a->cu_seqlens_q) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(a->cu_seqlens_k) & 3u) != 0)
+    return ATTN_ERR_LAYOUT;
+  if (!strides_ok(a->q_strides, 2, 2) || !strides_ok(a->o_strides, 2, 2) || !strides_ok(a->k_strides, 2, 2) ||
+      !strides_ok(a->v_strides, 2, 2))
+    return ATTN_ERR_LAYOUT;
+  if (a->total_q > kI32Max || a->total_k > kI32Max || a->B >= kI32Max) return ATTN_ERR_UNSUPPORTED;
+  if (a->total_k > 0 &&
+      (a->k_strides[0] >= attn_dev::kFwdMaxTokenStride || a->v_strides[0] >= attn_dev::kFwdMaxTokenStride))
+    return ATTN_ERR_UNSUPPORTED;
+  if (a->B * a->Hq * ((a->max_seqlen_q + 127) / 128) > kI32Max) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+extern "C" attn_status_t attn_fwd_varlen(const attn_fwd_varlen_args_t* a, void* stream) {
+  const attn_status_t st = attn_validate_fwd_varlen(a);
+  if (st != ATTN_OK) return st;
+  if (a->B == 0 || a->Hq == 0 || a->max_seqlen_q == 0) return ATTN_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  FwdParams p;
+  p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->o; p.lse = a->lse;
+  // the batch offset comes from the sequence offsets
+  p.q_sb = 0; p.q_sh = a->q_strides[1]; p.q_st = a->q_strides[0];
+  p.k_sb = 0; p.k_sh = a->k_strides[1]; p.k_st = a->k_strides[0];
+  p.v_sb = 0; p.v_sh = a->v_strides[1]; p.v_st = a->v_strides[0];
+  p.o_sb = 0; p.o_sh = a->o_strides[1]; p.o_st = a->o_strides[0];
+  p.Hq = (int)a->Hq;
+  p.Hkv = (int)a->Hkv;
+  p.group = (int)(a->Hq / a->Hkv);
+  p.Lq = (int)a->max_seqlen_q;  // sizes the grid; each sequence's own length is read on the device
+  p.Lk = 0;
+  p.lse_sb = 0;
+  p.lse_sh = a->total_q;
+  p.cu_q = a->cu_seqlens_q;
+  p.cu_k = a->cu_seqlens_k;
+  p.total_q = (int)a->total_q;
+  p.total_k = (int)a->total_k;
+  p.scale_log2 = effective_scale(a->scale, a->d) * kLog2e;
+  p.scale_log2_abs = std::fabs(p.scale_log2);
+  p.neg_q = p.scale_log2 < 0.f ? 1 : 0;
+  const int grid_x = (int)(a->B * a->Hq);
+  const bool c = a->causal != 0;
+  switch (a->d) {
+    case 64: return c ? launch_fwd_bf16<64, true>(p, grid_x, s) : launch_fwd_bf16<64, false>(p, grid_x, s);
+    case 80: return c ? launch_fwd_bf16<80, true>(p, grid_x, s) : launch_fwd_bf16<80, false>(p, grid_x, s);
+    case 128: return c ? launch_fwd_bf16<128, true>(p, grid_x, s) : launch_fwd_bf16<128, false>(p, grid_x, s);
   }
   return ATTN_ERR_UNSUPPORTED;
 }

@@ -24,9 +24,9 @@
 // read, visiting the keys of each 16-key slice in the score accumulator's row
 // order.
 //
-// Causal (top-left, Lq == Lk): key tiles entirely above a wave's last row are
-// skipped; tiles that straddle the diagonal or the end of the keys are masked
-// to -inf.  Key tile 0 is processed first and holds a visible key for every
+// Causal (top-left: query i sees keys j <= i, for any Lq and Lk): key tiles
+// entirely above a wave's last row are skipped; tiles that straddle the
+// diagonal or the end of the keys are masked to -inf.  Key tile 0 is processed first and holds a visible key for every
 // row, so the reference max is finite after each row's first tile.
 #pragma once
 
@@ -52,6 +52,14 @@ struct FwdParams {
   int Lq;
   int Lk;
   int n_qtiles;
+  // LSE element strides of (batch, head); the token stride is 1.
+  int64_t lse_sb, lse_sh;
+  // Packed sequences (NULL for the dense layout): sequence b's query rows are
+  // cu_q[b] .. cu_q[b+1]-1 of a [total_q, head, d] tensor, its keys cu_k[b] ..
+  // cu_k[b+1]-1; Lq then only sizes the grid (the longest sequence).
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
   float scale_log2;      // scale * log2(e)
   float scale_log2_abs;  // |scale * log2(e)|
   int neg_q;             // scale < 0: Q's sign bits are flipped on load (exact)
@@ -67,9 +75,28 @@ struct WorkItem {
   int b, h, hk, qt;
 };
 
+//
+// Packed sequences of different lengths make the work per item uneven across
+// sequences, so contiguous ranges would load the XCDs unevenly; there the
+// items go in hardware order with the query tile slowest, heaviest first
+// across all sequences (items past a sequence's end exit at once).
 __device__ __forceinline__ WorkItem prefill_work_item(const FwdParams& p, bool causal) {
   const int L = blockIdx.x;
   const int N = gridDim.x;
+  if (p.cu_q != nullptr) {
+    // L = ((qi * B + b) * Hkv + hk) * group + hg, with N = n_qtiles * B * Hq
+    const int nb = N / (p.n_qtiles * p.Hq);
+    WorkItem it;
+    const int hg = L % p.group;
+    int r = L / p.group;
+    it.hk = r % p.Hkv;
+    r /= p.Hkv;
+    it.b = r % nb;
+    const int qi = r / nb;
+    it.h = it.hk * p.group + hg;
+    it.qt = causal ? p.n_qtiles - 1 - qi : qi;
+    return it;
+  }
   const int full = N & ~7;
   int w = L;
   if (L < full) w = (L & 7) * (full >> 3) + (L >> 3);
@@ -167,7 +194,7 @@ static_assert(kSumGuard == float(1 << int(kRescaleLog2)), "guard is 2^kRescaleLo
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * Bf16FwdShape<D>::kWaves, Bf16FwdShape<D>::kGroupsPerCU) void
-attn_fwd_bf16_kernel(FwdParams p) {
+attn_fwd_bf16_kernel(FwdParams p_in) {
   using S = Bf16FwdShape<D>;
   constexpr int NB = S::kNB;
   typedef __attribute__((address_space(3))) char lds_char;
@@ -181,9 +208,25 @@ attn_fwd_bf16_kernel(FwdParams p) {
   const int lq = lane & 31;  // query column within a 32-query block (n index)
   const int g = lane >> 5;   // lane half
 
+  FwdParams p = p_in;
   const WorkItem wi = prefill_work_item(p, CAUSAL);
   const int b = wi.b, h = wi.h, hk = wi.hk;
   const int q0 = wi.qt * S::kBR;
+  // Packed sequences: this work item's sequence, its bounds clamped to the
+  // packed extents (inconsistent offsets then cannot reach past the buffers).
+  // Work items past the end of a shorter sequence have nothing to do.
+  if (p.cu_q != nullptr) {
+    const int qs = min(max(p.cu_q[b], 0), p.total_q), qe = min(max(p.cu_q[b + 1], qs), p.total_q);
+    const int ks = min(max(p.cu_k[b], 0), p.total_k), ke = min(max(p.cu_k[b + 1], ks), p.total_k);
+    p.Lq = qe - qs;
+    p.Lk = ke - ks;
+    p.q = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)qs * p.q_st;
+    p.o = reinterpret_cast<uint16_t*>(p.o) + (int64_t)qs * p.o_st;
+    p.lse += qs;
+    p.k = reinterpret_cast<const uint16_t*>(p.k) + (int64_t)ks * p.k_st;
+    p.v = reinterpret_cast<const uint16_t*>(p.v) + (int64_t)ks * p.v_st;
+  }
+  if (q0 >= p.Lq) return;
   const int row0 = q0 + wave * S::kRowsPerWave;  // first query row of this wave
   int qrow[NB];
 #pragma unroll
@@ -514,7 +557,7 @@ attn_fwd_bf16_kernel(FwdParams p) {
         }
       if (g == 0) {
         const float lse = l_tot > 0.f ? (m_run[nb] + log2f(l_tot)) * kLn2 : kNegInf;
-        p.lse[((int64_t)b * p.Hq + h) * p.Lq + qrow[nb]] = lse;
+        p.lse[b * p.lse_sb + h * p.lse_sh + qrow[nb]] = lse;
       }
     }
   }

@@ -81,7 +81,7 @@ def test_fwd_valid_configurations(d, dtype, causal):
     (dict(q=0), NULL), (dict(o=0), NULL), (dict(lse=0), NULL), (dict(k=0), NULL), (dict(v=0), NULL),
     (dict(dtype=2), DTYPE), (dict(dtype=-1), DTYPE),
     (dict(B=-1), SHAPE), (dict(Lq=-5), SHAPE), (dict(Hkv=0), SHAPE), (dict(Hq=8, Hkv=3), SHAPE),
-    (dict(causal=1, Lq=300, Lk=200), SHAPE), (dict(scale=float("nan")), SHAPE),
+    (dict(scale=float("nan")), SHAPE),
     (dict(scale=float("inf")), SHAPE),
     (dict(d=96), UNSUP), (dict(d=32), UNSUP), (dict(d=256), UNSUP), (dict(d=0), UNSUP),
     (dict(q=P + 8), LAYOUT), (dict(k=P + 2), LAYOUT), (dict(lse=P + 4), LAYOUT),
@@ -110,7 +110,14 @@ def test_fwd_empty_inputs_are_valid_noops():
     assert vfwd(Lq=0) == OK and run_fwd(Lq=0) == OK
     # no keys: valid (O = 0, LSE = -inf); k and v may be NULL then
     assert vfwd(Lk=0, k=0, v=0) == OK
-    assert vfwd(Lk=0, causal=1) == SHAPE
+    assert vfwd(Lk=0, causal=1, k=0, v=0) == OK
+
+
+@pytest.mark.parametrize("Lq,Lk", [(300, 200), (200, 300), (1, 4096), (4096, 1)])
+def test_fwd_cross_attention_shapes_are_valid(Lq, Lk):
+    # Lq != Lk (cross-attention), causal or not; causal is top-left (j <= i)
+    for causal in (0, 1):
+        assert vfwd(Lq=Lq, Lk=Lk, causal=causal) == OK
 
 
 def test_fwd_null_struct():
@@ -194,3 +201,53 @@ def test_build_entry_point_exists():
     import importlib
     ge = importlib.import_module("__graft_entry__")
     assert callable(ge.build) and callable(ge.smoke)
+
+
+def var_args(**kw):
+    a = sdpa.FwdVarlenArgs()
+    B, Hq, Hkv, tq, tk, mq, d = (kw.get("B", 3), kw.get("Hq", 8), kw.get("Hkv", 2), kw.get("total_q", 500),
+                                 kw.get("total_k", 700), kw.get("max_seqlen_q", 300), kw.get("d", 128))
+    a.q, a.k, a.v, a.o, a.lse, a.cu_seqlens_q, a.cu_seqlens_k = [
+        kw.get(n, P + i * 0x10000000) for i, n in
+        enumerate(("q", "k", "v", "o", "lse", "cu_seqlens_q", "cu_seqlens_k"))]
+    a.B, a.Hq, a.Hkv, a.total_q, a.total_k, a.max_seqlen_q, a.d = B, Hq, Hkv, tq, tk, mq, d
+    a.q_strides = sdpa._i64x2(*kw.get("qs", (Hq * d, d)))
+    a.k_strides = sdpa._i64x2(*kw.get("ks", (Hkv * d, d)))
+    a.v_strides = sdpa._i64x2(*kw.get("vs", (Hkv * d, d)))
+    a.o_strides = sdpa._i64x2(*kw.get("os", (Hq * d, d)))
+    a.dtype = kw.get("dtype", sdpa.ATTN_BF16)
+    a.causal = kw.get("causal", 0)
+    a.scale = kw.get("scale", 0.0)
+    return a
+
+
+def vvar(**kw):
+    return sdpa.lib().attn_validate_fwd_varlen(ctypes.byref(var_args(**kw)))
+
+
+@pytest.mark.parametrize("d", [64, 80, 128])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_varlen_valid(d, causal):
+    assert vvar(d=d, causal=causal) == OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), NULL), (dict(cu_seqlens_q=0), NULL), (dict(cu_seqlens_k=0), NULL), (dict(lse=0), NULL),
+    (dict(k=0), NULL), (dict(dtype=1), UNSUP), (dict(dtype=5), DTYPE), (dict(d=96), UNSUP),
+    (dict(Hkv=3), SHAPE), (dict(B=-1), SHAPE), (dict(max_seqlen_q=501), SHAPE), (dict(total_k=-1), SHAPE),
+    (dict(scale=float("inf")), SHAPE),
+    (dict(q=P + 8), LAYOUT), (dict(cu_seqlens_k=P + 2), LAYOUT), (dict(qs=(8 * 128 + 4, 128)), LAYOUT),
+    (dict(ks=(2 ** 28, 128)), UNSUP), (dict(total_q=2 ** 31, max_seqlen_q=10), UNSUP),
+])
+def test_varlen_rejections(kw, status):
+    assert vvar(**kw) == status
+    assert sdpa.lib().attn_fwd_varlen(ctypes.byref(var_args(**kw)), None) == status
+
+
+def test_varlen_empty_is_noop():
+    L = sdpa.lib()
+    for kw in (dict(B=0), dict(Hq=0, Hkv=0), dict(max_seqlen_q=0)):
+        assert vvar(**kw) == OK and L.attn_fwd_varlen(ctypes.byref(var_args(**kw)), None) == OK
+    # no keys at all: k and v may be NULL (every row gets O = 0, LSE = -inf)
+    assert vvar(total_k=0, k=0, v=0) == OK
+    assert L.attn_validate_fwd_varlen(None) == NULL

@@ -11,6 +11,9 @@ Recipe (one per workload):
                   torch's own conversion); the oracle receives exactly those
                   values widened to float64
   decode workloads, after V: lengths = randint(lo, hi + 1, (B,), generator=g)
+  packed variable-length workloads: lengths = randint(lo, hi + 1, (B,),
+                  generator=g) first (query and key lengths equal unless
+                  given), then Q [total_q, Hq, d], K, V [total_k, Hkv, d]
 
 The five named workloads are the shapes the attention pages discuss:
 the GPT-3-scale layer (B=1, 96 heads, n=4096, d=64) from "Flash Attention原理"
@@ -70,6 +73,29 @@ C3 = FwdWorkload("fwd_bf16_causal_b4_h16_n2048_d80", 4, 16, 16, 2048, 2048, 80, 
 C4 = FwdWorkload("fwd_bf16_causal_gqa_b1_hq32_hkv8_n8192_d128", 1, 32, 8, 8192, 8192, 128, "bf16", True, 1004)
 C5 = DecodeWorkload("decode_bf16_gqa_b64_hq32_hkv8_lmax8192_d128", 64, 32, 8, 8192, 128, 1024, 8192, "bf16", 1005)
 
+
+
+@dataclass(frozen=True)
+class VarlenWorkload:
+    """Packed sequences of random lengths (cnblogs FAQ Q10): the serving-prefill
+    shape, one kernel over sequences of different lengths without padding."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    len_lo: int
+    len_hi: int          # inclusive
+    d: int
+    dtype: str
+    causal: bool
+    seed: int
+
+
+# Packed causal GQA prefill of 16 sequences of 256..4096 tokens at the n=8192
+# workload's head shape.
+C6 = VarlenWorkload("varlen_bf16_causal_gqa_b16_hq32_hkv8_len256_4096_d128", 16, 32, 8, 256, 4096, 128,
+                    "bf16", True, 1006)
+
 FWD_WORKLOADS = {w.name: w for w in (C1, C2, C3, C4)}
 DECODE_WORKLOADS = {C5.name: C5}
 
@@ -118,6 +144,23 @@ def make_decode_inputs(w: DecodeWorkload, poison_tail: bool = False,
     return q, k, v, lens
 
 
+def make_varlen_inputs(w: VarlenWorkload, lens_q=None, lens_k=None):
+    """q [total_q,Hq,d], k and v [total_k,Hkv,d] in the workload's dtype and the
+    int32 offsets cu_q, cu_k [B+1] on the CPU.  Lengths are drawn first (query
+    and key lengths equal) unless given."""
+    g = torch.Generator().manual_seed(w.seed)
+    lens = torch.randint(w.len_lo, w.len_hi + 1, (w.B,), generator=g, dtype=torch.int64)
+    lq = torch.as_tensor(lens_q, dtype=torch.int64) if lens_q is not None else lens
+    lk = torch.as_tensor(lens_k, dtype=torch.int64) if lens_k is not None else lq
+    cu_q = torch.cat([torch.zeros(1, dtype=torch.int64), torch.cumsum(lq, 0)]).to(torch.int32)
+    cu_k = torch.cat([torch.zeros(1, dtype=torch.int64), torch.cumsum(lk, 0)]).to(torch.int32)
+    q = torch.randn((int(cu_q[-1]), w.Hq, w.d), generator=g, dtype=torch.float32)
+    k = torch.randn((int(cu_k[-1]), w.Hkv, w.d), generator=g, dtype=torch.float32)
+    v = torch.randn((int(cu_k[-1]), w.Hkv, w.d), generator=g, dtype=torch.float32)
+    dt = torch_dtype(w.dtype)
+    return q.to(dt), k.to(dt), v.to(dt), cu_q, cu_k
+
+
 def shrink(w, **kw):
     """A copy of a workload with some sizes replaced (name and seed kept unless given)."""
     return replace(w, **kw)
@@ -140,6 +183,16 @@ def algorithmic_bytes_fwd(B, Hq, Hkv, Lq, Lk, d, elem_bytes) -> int:
     六); S and P never leave the chip.
     """
     return (B * Hq * Lq * d * 2 + B * Hkv * Lk * d * 2) * elem_bytes + B * Hq * Lq * 4
+
+
+def algorithmic_flops_varlen(lens_q, lens_k, Hq, d, causal) -> int:
+    """Sum over sequences of the dense count; causal credited as exactly half."""
+    return sum(algorithmic_flops_fwd(1, Hq, int(a), int(b), d, causal) for a, b in zip(lens_q, lens_k))
+
+
+def algorithmic_bytes_varlen(total_q, total_k, Hq, Hkv, d, elem_bytes, B) -> int:
+    """Q, K, V read once, O written once, LSE once, plus the two offset arrays."""
+    return algorithmic_bytes_fwd(1, Hq, Hkv, total_q, total_k, d, elem_bytes) + 2 * (B + 1) * 4
 
 
 def algorithmic_flops_decode(seqlens, Hq, d, Lmax) -> int:
