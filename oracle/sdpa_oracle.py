@@ -31,7 +31,13 @@ notes):
   * a grouped-query head h reads key/value head h // (Hq / Hkv);
   * decode is one query token per sequence that sees cache slots 0..L_b-1;
     a length above the cache size is clamped to it;
-  * a row that sees no key at all gets O = 0 and LSE = -inf.
+  * a row that sees no key at all gets O = 0 and LSE = -inf;
+  * the backward pass (cnblogs section 五: the forward keeps only the row
+    statistics and the backward recomputes the softmax values from them) is
+    the textbook chain rule through S, P and O, which the pages do not write
+    out: dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(P * dP)),
+    dQ = scale dS K, dK = scale dS^T Q; a grouped key/value head receives the
+    sum over its query heads.
 
 All functions take and return numpy float64 arrays.
 """
@@ -163,6 +169,56 @@ def attention_forward(q, k, v, causal: bool = False, scale: Optional[float] = No
     if return_sp:
         return o, lse, s_all, p_all
     return o, lse
+
+
+def _head_backward(q, k, v, do, scale: float, causal: bool):
+    """Gradients for one (batch, query head): q, do [Lq, d]; k, v [Lk, d].
+
+    Recomputes S and P as the forward defines them, then applies the chain
+    rule step by step.  Returns dq [Lq, d], dk [Lk, d], dv [Lk, d].
+    """
+    lq, lk = q.shape[0], k.shape[0]
+    if lk == 0 or lq == 0:
+        return np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    _, _, s, p = _head_attention(q, k, v, scale, causal, return_sp=True)
+    dv = p.T @ do                                    # O = P V
+    dp = do @ v.T
+    dsum = (p * dp).sum(axis=-1, keepdims=True)      # softmax along keys
+    ds = p * (dp - dsum)
+    dq = (ds @ k) * scale                            # S = Q K^T * scale
+    dk = (ds.T @ q) * scale
+    return dq, dk, dv
+
+
+def attention_backward(q, k, v, do, causal: bool = False, scale: Optional[float] = None,
+                       threads: Optional[int] = None):
+    """Gradients of the prefill attention output O with respect to q, k, v
+    for the output gradient do [B,Hq,Lq,d].  Returns dq [B,Hq,Lq,d],
+    dk and dv [B,Hkv,Lk,d] (each kv head summed over its query heads)."""
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    B, Hq, Lq, d = q.shape
+    Hkv = k.shape[1]
+    if do.shape != q.shape or k.shape[0] != B or v.shape != k.shape:
+        raise ValueError("q, k, v, do shapes disagree")
+    if Hkv == 0 or Hq % Hkv != 0:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    if scale is None:
+        scale = default_scale(d)
+    group = Hq // Hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    items = [(b, h) for b in range(B) for h in range(Hq)]
+
+    def one(item):
+        b, h = item
+        return _head_backward(q[b, h], k[b, h // group], v[b, h // group], do[b, h], scale, causal)
+
+    for (b, h), (gq, gk, gv) in zip(items, _pool_map(one, items, threads)):
+        dq[b, h] = gq
+        dk[b, h // group] += gk
+        dv[b, h // group] += gv
+    return dq, dk, dv
 
 
 def attention_forward_varlen(q, k, v, cu_q: Sequence[int], cu_k: Sequence[int], causal: bool = False,

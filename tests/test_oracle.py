@@ -373,6 +373,67 @@ def test_varlen_single_sequence_is_dense():
     assert np.array_equal(ov, o[0].transpose(1, 0, 2)) and np.array_equal(lv, lse[0])
 
 
+# --------------------------------------------------- P-16 backward pass
+def _loss(q, k, v, w, causal):
+    o, _ = orc.attention_forward(q, k, v, causal=causal)
+    return float((o * w).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Lq,Lk", [(5, 5), (4, 7)])
+def test_backward_matches_finite_differences(causal, Lq, Lk):
+    """Central differences of sum(O * W) need no derivation at all."""
+    q, k, v = rnd((1, 2, Lq, 4), 120), rnd((1, 1, Lk, 4), 121), rnd((1, 1, Lk, 4), 122)
+    w = rnd((1, 2, Lq, 4), 123)
+    dq, dk, dv = orc.attention_backward(q, k, v, w, causal=causal)
+    eps = 1e-6
+    rng = np.random.default_rng(124)
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, n)) for n in x.shape)
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = _loss(args["q"], args["k"], args["v"], w, causal)
+            args[name] = xm
+            lm = _loss(args["q"], args["k"], args["v"], w, causal)
+            assert abs((lp - lm) / (2 * eps) - g[idx]) <= 1e-7, (name, idx)
+
+
+@pytest.mark.parametrize("causal,Hq,Hkv,Lq,Lk", [(False, 4, 4, 33, 33), (True, 4, 4, 33, 33),
+                                                 (True, 8, 2, 20, 29), (False, 8, 2, 29, 20)])
+def test_backward_matches_torch_autograd_float64(causal, Hq, Hkv, Lq, Lk):
+    q, k, v = rnd((2, Hq, Lq, 16), 125, 2.0), rnd((2, Hkv, Lk, 16), 126), rnd((2, Hkv, Lk, 16), 127)
+    do = rnd((2, Hq, Lq, 16), 128)
+    dq, dk, dv = orc.attention_backward(q, k, v, do, causal=causal)
+    tq = torch.from_numpy(q).requires_grad_()
+    tk = torch.from_numpy(k).requires_grad_()
+    tv = torch.from_numpy(v).requires_grad_()
+    g = Hq // Hkv
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk.repeat_interleave(g, 1),
+                                                         tv.repeat_interleave(g, 1), is_causal=causal)
+    o.backward(torch.from_numpy(do))
+    assert np.abs(dq - tq.grad.numpy()).max() <= 1e-12
+    assert np.abs(dk - tk.grad.numpy()).max() <= 1e-12
+    assert np.abs(dv - tv.grad.numpy()).max() <= 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_invariants(causal):
+    q, k, v, do = rnd((1, 2, 11, 8), 129), rnd((1, 2, 11, 8), 130), rnd((1, 2, 11, 8), 131), rnd((1, 2, 11, 8), 132)
+    dq, dk, dv = orc.attention_backward(q, k, v, do, causal=causal)
+    # each score row's dS sums to zero, so the key gradients sum to zero over keys
+    assert np.abs(dk.sum(axis=2)).max() <= 1e-12
+    # each probability row sums to one, so the value gradients sum to the output gradients
+    assert np.abs(dv.sum(axis=2) - do.sum(axis=2)).max() <= 1e-12
+    # identical value rows make O independent of the scores: no gradient reaches Q or K
+    vc = np.broadcast_to(v[:, :, :1], v.shape).copy()
+    dq0, dk0, _ = orc.attention_backward(q, k, vc, do, causal=causal)
+    assert np.abs(dq0).max() <= 1e-12 and np.abs(dk0).max() <= 1e-12
+
+
 # -------------------------------------------- planted mistakes are caught
 def _mutant(kind):
     """Copies of the oracle's per-head step with one plausible slip each."""
@@ -415,3 +476,34 @@ def test_planted_mistakes(monkeypatch, kind):
         except AssertionError:
             failures += 1
     assert failures >= 1, f"planted mistake {kind} not caught"
+
+
+def _backward_mutant(kind):
+    """Copies of the oracle's per-head backward with one plausible slip each."""
+    def f(q, k, v, do, scale, causal):
+        lq, lk = q.shape[0], k.shape[0]
+        if lk == 0 or lq == 0:
+            return np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+        _, _, s, p = orc._head_attention(q, k, v, scale, causal, return_sp=True)
+        dv = (p.T @ do) if kind != "dv_untransposed" else (p[:lk, :lq] @ do[:lk]) if lq == lk else p.T @ do * 2
+        dp = do @ v.T
+        dsum = (p * dp).sum(axis=-1, keepdims=True) if kind != "no_softmax_correction" else 0.0
+        ds = p * (dp - dsum)
+        dq = (ds @ k) * (scale if kind != "dq_no_scale" else 1.0)
+        dk = (ds.T @ q) * scale if kind != "dk_from_dq_side" else (ds @ q[:lk]) * scale if lq == lk else ds.T @ q
+        return dq, dk, dv
+    return f
+
+
+@pytest.mark.parametrize("kind", ["dv_untransposed", "no_softmax_correction", "dq_no_scale", "dk_from_dq_side"])
+def test_planted_backward_mistakes(monkeypatch, kind):
+    monkeypatch.setattr(orc, "_head_backward", _backward_mutant(kind))
+    failures = 0
+    for fn in (lambda: test_backward_matches_finite_differences(True, 5, 5),
+               lambda: test_backward_matches_torch_autograd_float64(True, 4, 4, 33, 33),
+               lambda: test_backward_invariants(False)):
+        try:
+            fn()
+        except AssertionError:
+            failures += 1
+    assert failures >= 1, f"planted backward mistake {kind} not caught"
