@@ -7,8 +7,9 @@ One step = one pass of the whole path over synthetic, HBM-resident inputs:
 Each call is timed with HIP events recorded on the stream the kernels run on;
 the step as a whole is timed with host clocks between device synchronisations.
 After the step loop, attn_fwd_varlen on 16 packed causal GQA sequences of
-256..4096 tokens (d=128) is timed the same way on its own and reported in
-`extra` (it is not part of the step).
+256..4096 tokens (d=128) and attn_bwd on the causal GQA n=8192 d=128 workload
+are timed the same way, each on its own, and reported in `extra` (they are not
+part of the step).
 
 Prints ONE JSON line.  `value` is the headline workload's attention-forward
 throughput in TFLOP/s (credited flops 4 n^2 d H B, halved when causal).
@@ -35,7 +36,7 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak (256 CU x 2.4 GHz x 
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E peak
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "scaled_dot_product_qk_amd", "csrc", f)
-                  for f in ("attn_api.hip", "device_common.h", "fwd_bf16.h", "fwd_f32.h", "decode.h")]
+                  for f in ("attn_api.hip", "device_common.h", "fwd_bf16.h", "fwd_f32.h", "decode.h", "bwd_bf16.h")]
 
 
 def kernel_source_hash() -> str:
@@ -71,7 +72,7 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "fwd_n4096", "fwd_causal_n8192", "decode", "fwd_varlen"],
+    ap.add_argument("--only", choices=["all", "fwd_n4096", "fwd_causal_n8192", "decode", "fwd_varlen", "bwd"],
                     default="all",
                     help="time one call of the step only (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -126,8 +127,10 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     names = ["fwd_n4096", "fwd_causal_n8192", "decode"] if args.only == "all" else \
-        ([] if args.only == "fwd_varlen" else [args.only])
+        ([] if args.only in ("fwd_varlen", "bwd") else [args.only])
     with_varlen = args.only in ("all", "fwd_varlen")
+    with_bwd = args.only in ("all", "bwd")
+    solo = (["fwd_varlen"] if with_varlen else []) + (["bwd"] if with_bwd else [])
 
     # ---- inputs, generated on the host and copied once to HBM ----
     calls = {}
@@ -161,10 +164,21 @@ def main():
         lv = torch.empty((wl.C6.Hq, GV[0].shape[0]), dtype=torch.float32, device=dev)
         calls["fwd_varlen"] = lambda: sdpa.attn_fwd_varlen(*GV, max(lens_v), causal=True, out=ov, lse=lv,
                                                            stream=stream)
+    if with_bwd:
+        qb, kb, vb = wl.make_fwd_inputs(wl.C4)
+        gdo = torch.Generator().manual_seed(wl.C4.seed + 50)
+        dob = torch.randn(qb.shape, generator=gdo, dtype=torch.float32).to(qb.dtype)
+        GB = [t.to(dev) for t in (qb, kb, vb, dob)]
+        del qb, kb, vb, dob
+        ob, lb = sdpa.attn_fwd(GB[0], GB[1], GB[2], causal=True, stream=stream)
+        dqb, dkb, dvb = torch.empty_like(GB[0]), torch.empty_like(GB[1]), torch.empty_like(GB[2])
+        wsb = torch.empty(sdpa.attn_bwd_workspace_bytes(wl.C4.B, wl.C4.Hq, wl.C4.Lq), dtype=torch.uint8, device=dev)
+        calls["bwd"] = lambda: sdpa.attn_bwd(GB[0], GB[1], GB[2], ob, lb, GB[3], causal=True, dq=dqb, dk=dkb,
+                                             dv=dvb, workspace=wsb, stream=stream)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
-        for n in names + (["fwd_varlen"] if with_varlen else []):
+        for n in names + solo:
             calls[n]()
     torch.cuda.synchronize()
 
@@ -181,15 +195,15 @@ def main():
             ev[n].append((a, b))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    if with_varlen:  # timed on its own, outside the step
-        ev["fwd_varlen"] = []
+    for n in solo:  # each timed on its own, outside the step
+        ev[n] = []
         for _ in range(args.steps):
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            calls["fwd_varlen"]()
+            calls[n]()
             b.record(stream)
-            ev["fwd_varlen"].append((a, b))
+            ev[n].append((a, b))
         torch.cuda.synchronize()
     ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / len(ev[n]) for n in ev}
 
@@ -221,6 +235,14 @@ def main():
         res["fwd_varlen"] = {"kernel": "attn_fwd_bf16_d128_causal (packed sequences)", "ms": ms["fwd_varlen"],
                              "tflops": fv / t / 1e12, "algorithmic_flops": fv,
                              "total_tokens": int(sum(lens_v)), "sequences": C6.B}
+
+    if "bwd" in ms:
+        t = ms["bwd"] / 1e3
+        fb = wl.algorithmic_flops_bwd(C4.B, C4.Hq, C4.Lq, C4.Lk, C4.d, C4.causal)
+        res["bwd"] = {"kernel": "attn_bwd_delta_kernel<128> + attn_bwd_dkdv_kernel<128, true> + "
+                                "attn_bwd_dq_kernel<128, true>", "ms": ms["bwd"], "tflops": fb / t / 1e12,
+                      "algorithmic_flops": fb,
+                      "algorithmic_bytes": wl.algorithmic_bytes_bwd(C4.B, C4.Hq, C4.Hkv, C4.Lq, C4.Lk, C4.d, 2)}
 
     def roof_fwd(r, tag):
         tr = counted_traffic(tag)
@@ -257,6 +279,9 @@ def main():
     if "fwd_varlen" in res:
         r = res["fwd_varlen"]
         out["extra"]["fwd_varlen_causal_gqa_b16_d128"] = dict(r, roofline=roof_fwd(r, "attn_fwd_varlen_d128_causal_b16"))
+    if "bwd" in res:
+        r = res["bwd"]
+        out["extra"]["bwd_causal_gqa_n8192_d128"] = dict(r, roofline=roof_fwd(r, "attn_bwd_d128_causal_n8192"))
     if headline:
         out["extra"]["fwd_n4096_d64"] = headline
     if not args.no_cpu_baseline and args.only in ("all", "fwd_n4096"):

@@ -121,7 +121,33 @@ typedef struct {
   float scale;     /* multiplier of Q K^T; 0 selects 1/sqrt(d) */
 } attn_fwd_varlen_args_t;
 
-/* Decode: one query token per sequence against a ragged KV cache. */
+/* Backward of the prefill ("Flash Attention原理：分块计算与重计算" (cnblogs),
+ * section 五: the probabilities are recomputed from the stored log-sum-exp). */
+typedef struct {
+  const void *q;     /* [B, Hq,  Lq, d]  the forward's inputs ... */
+  const void *k;     /* [B, Hkv, Lk, d] */
+  const void *v;     /* [B, Hkv, Lk, d] */
+  const void *o;     /* [B, Hq,  Lq, d]  ... its output O ... */
+  const void *dout;  /* [B, Hq,  Lq, d]  ... and the gradient of the loss with respect to O */
+  const float *lse;  /* [B, Hq, Lq] fp32 contiguous, as attn_fwd returned it */
+  void *dq;          /* [B, Hq,  Lq, d]  outputs, same dtype as q */
+  void *dk;          /* [B, Hkv, Lk, d]  a grouped kv head gets the sum over its query heads */
+  void *dv;          /* [B, Hkv, Lk, d] */
+  int64_t B, Hq, Hkv, Lq, Lk, d;
+  int64_t q_strides[3];  /* element strides of (batch, head, token); d stride is 1 */
+  int64_t k_strides[3];
+  int64_t v_strides[3];
+  int64_t o_strides[3];
+  int64_t do_strides[3];
+  int64_t dq_strides[3];
+  int64_t dk_strides[3];
+  int64_t dv_strides[3];
+  int32_t dtype;   /* attn_dtype_t; ATTN_BF16 */
+  int32_t causal;  /* as in the forward (top-left) */
+  float scale;     /* as in the forward; 0 selects 1/sqrt(d) */
+} attn_bwd_args_t;
+
+/* Decode: one query token per sequence against a ragged KV cache. *//* Decode: one query token per sequence against a ragged KV cache. */
 typedef struct {
   const void *q;          /* [B, Hq, d] */
   const void *k_cache;    /* [B, Hkv, Lmax, d]; slots >= seqlens[b] are never read */
@@ -190,10 +216,33 @@ size_t attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Lmax, int64_t 
 attn_status_t attn_decode(const attn_decode_args_t *args, void *workspace,
                           size_t workspace_bytes, void *stream);
 
+/*
+ * attn_bwd_workspace_bytes - bytes of device workspace attn_bwd needs (one
+ * fp32 per query row: D = rowsum(dO * O)).  Returns 0 for invalid sizes.
+ */
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq);
+
+/*
+ * attn_bwd - gradients dQ, dK, dV of the prefill attention, recomputing the
+ * probabilities from the stored LSE: dV = P^T dO, dP = dO V^T,
+ * dS = P * (dP - rowsum(dO * O)), dQ = scale dS K, dK = scale dS^T Q.  Three
+ * kernels are enqueued (row sums, dK/dV, dQ); nothing is accumulated with
+ * atomics, so results are deterministic.  `workspace` is caller-owned device
+ * memory of at least attn_bwd_workspace_bytes(B, Hq, Lq) bytes, 256-byte
+ * aligned, contents irrelevant on entry.
+ * Supported: dtype bf16; d in {64, 128}; Hq % Hkv == 0; Lq and Lk
+ * independent; causal or not.  dK and dV of keys that no query sees are 0;
+ * Lq == 0 gives dK = dV = 0.  B == 0, Hq == 0 or Lq == Lk == 0 is a no-op.
+ */
+attn_status_t attn_bwd(const attn_bwd_args_t *args, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
 /* Argument checks only (no device work, no HIP call): the status attn_fwd /
+ * attn_decode would return before launching.  Usable without a GPU. *//* Argument checks only (no device work, no HIP call): the status attn_fwd /
  * attn_decode would return before launching.  Usable without a GPU. */
 attn_status_t attn_validate_fwd(const attn_fwd_args_t *args);
 attn_status_t attn_validate_fwd_varlen(const attn_fwd_varlen_args_t *args);
+attn_status_t attn_validate_bwd(const attn_bwd_args_t *args);
 attn_status_t attn_validate_decode(const attn_decode_args_t *args);
 
 /* Static, human-readable name of a status code. */

@@ -221,6 +221,42 @@ def attention_backward(q, k, v, do, causal: bool = False, scale: Optional[float]
     return dq, dk, dv
 
 
+def attention_backward_sampled(q, k, v, do, b: int, hk: int, q_rows: Iterable[int], keys: Iterable[int],
+                               causal: bool = False, scale: Optional[float] = None):
+    """The backward's definition for a few outputs of one (batch, kv head), at
+    any size: dQ of the given query rows for every query head of the group, and
+    dK, dV of the given keys (summed over the group).  Each query head's full
+    score matrix is formed once (n x n float64), then only the asked-for rows
+    and columns of the chain rule are evaluated.
+    Returns dq [group, len(q_rows), d], dk and dv [len(keys), d]."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    group = Hq // Hkv
+    d = q.shape[-1]
+    if scale is None:
+        scale = default_scale(d)
+    q_rows = np.asarray(list(q_rows), dtype=np.int64)
+    keys = np.asarray(list(keys), dtype=np.int64)
+    kk, vv = _as64(k[b, hk]), _as64(v[b, hk])
+    dq = np.zeros((group, len(q_rows), d))
+    dk = np.zeros((len(keys), d))
+    dv = np.zeros((len(keys), vv.shape[1]))
+    for hg in range(group):
+        h = hk * group + hg
+        qq, dd = _as64(q[b, h]), _as64(do[b, h])
+        o, _, s, p = _head_attention(qq, kk, vv, scale, causal, return_sp=True)
+        drow = (dd * o).sum(axis=-1)                 # rowsum(P * dP) = rowsum(dO * O)
+        # dQ rows: dS of those rows over all keys
+        dp_r = dd[q_rows] @ vv.T
+        ds_r = p[q_rows] * (dp_r - drow[q_rows, None])
+        dq[hg] = (ds_r @ kk) * scale
+        # dK, dV of the sampled keys: those columns over all queries
+        dp_c = dd @ vv[keys].T
+        ds_c = p[:, keys] * (dp_c - drow[:, None])
+        dk += (ds_c.T @ qq) * scale
+        dv += p[:, keys].T @ dd
+    return dq, dk, dv
+
+
 def attention_forward_varlen(q, k, v, cu_q: Sequence[int], cu_k: Sequence[int], causal: bool = False,
                              scale: Optional[float] = None, threads: Optional[int] = None):
     """Packed variable-length prefill (cnblogs FAQ Q10, cross-attention FAQ Q15).

@@ -20,9 +20,10 @@ ATTN_BF16, ATTN_F32 = 0, 1
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_DTYPE",
                 4: "ATTN_ERR_LAYOUT", 5: "ATTN_ERR_UNSUPPORTED", 6: "ATTN_ERR_WORKSPACE",
                 7: "ATTN_ERR_HIP"}
-EXPORTED = ("attn_fwd", "attn_fwd_varlen", "attn_decode", "attn_decode_workspace_bytes",
-            "attn_validate_fwd", "attn_validate_fwd_varlen", "attn_validate_decode", "attn_status_str",
-            "attn_kernel_name", "attn_version")
+EXPORTED = ("attn_fwd", "attn_fwd_varlen", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode",
+            "attn_decode_workspace_bytes", "attn_validate_fwd", "attn_validate_fwd_varlen",
+            "attn_validate_bwd", "attn_validate_decode", "attn_status_str", "attn_kernel_name",
+            "attn_version")
 
 _i64 = ctypes.c_int64
 _i64x3 = _i64 * 3
@@ -46,6 +47,17 @@ class FwdVarlenArgs(ctypes.Structure):
                 ("max_seqlen_q", _i64), ("d", _i64),
                 ("q_strides", _i64x2), ("k_strides", _i64x2), ("v_strides", _i64x2),
                 ("o_strides", _i64x2),
+                ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class BwdArgs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("o", ctypes.c_void_p), ("dout", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+                ("B", _i64), ("Hq", _i64), ("Hkv", _i64), ("Lq", _i64), ("Lk", _i64), ("d", _i64),
+                ("q_strides", _i64x3), ("k_strides", _i64x3), ("v_strides", _i64x3),
+                ("o_strides", _i64x3), ("do_strides", _i64x3), ("dq_strides", _i64x3),
+                ("dk_strides", _i64x3), ("dv_strides", _i64x3),
                 ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
@@ -83,6 +95,12 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_varlen.restype = ctypes.c_int
         L.attn_validate_fwd_varlen.argtypes = [ctypes.POINTER(FwdVarlenArgs)]
         L.attn_validate_fwd_varlen.restype = ctypes.c_int
+        L.attn_bwd.argtypes = [ctypes.POINTER(BwdArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.attn_bwd.restype = ctypes.c_int
+        L.attn_validate_bwd.argtypes = [ctypes.POINTER(BwdArgs)]
+        L.attn_validate_bwd.restype = ctypes.c_int
+        L.attn_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64]
+        L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.attn_kernel_name.argtypes = [ctypes.POINTER(FwdArgs)]
         L.attn_kernel_name.restype = ctypes.c_char_p
         L.attn_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p, ctypes.c_size_t,
@@ -238,6 +256,56 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, caus
     if st != 0:
         raise AttnError(st, "attn_fwd_varlen")
     return out, lse
+
+
+def attn_bwd_workspace_bytes(B: int, Hq: int, Lq: int) -> int:
+    return int(lib().attn_bwd_workspace_bytes(B, Hq, Lq))
+
+
+def make_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, causal: bool, scale: Optional[float]) -> BwdArgs:
+    a = BwdArgs()
+    a.q, a.k, a.v, a.o, a.dout = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr()
+    a.lse, a.dq, a.dk, a.dv = lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    a.B, a.Hq, a.Lq, a.d = q.shape
+    a.Hkv, a.Lk = k.shape[1], k.shape[2]
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        setattr(a, f"{name}_strides", _i64x3(*t.stride()[:3]))
+    a.dtype = _dtype_code(q)
+    a.causal = 1 if causal else 0
+    a.scale = 0.0 if scale is None else float(scale)
+    return a
+
+
+def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: Optional[float] = None, dq=None, dk=None,
+             dv=None, workspace=None, stream=None):
+    """dQ, dK, dV of attention for the output gradient dout, recomputing the
+    probabilities from lse (as attn_fwd returned it for q, k, v, o)."""
+    import torch
+    _check_fwd_tensors(q, k, v)
+    _check_device(q, o, lse, dout)
+    for t in (o, dout):
+        if t.shape != q.shape or t.dtype != q.dtype or (t.numel() and t.stride(3) != 1):
+            raise ValueError("o and dout must match q's shape and dtype with a contiguous head_dim")
+    B, Hq, Lq, d = q.shape
+    if lse.shape != (B, Hq, Lq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be the contiguous float32 [B, Hq, Lq] tensor attn_fwd returned")
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    _check_device(q, dq, dk, dv)
+    for t, ref in ((dq, q), (dk, k), (dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype or (t.numel() and t.stride(3) != 1):
+            raise ValueError("gradients must match their inputs' shapes and dtypes with a contiguous head_dim")
+    need = attn_bwd_workspace_bytes(B, Hq, Lq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_device(q, workspace)
+    args = make_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, causal, scale)
+    st = lib().attn_bwd(ctypes.byref(args), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                        _stream_handle(stream))
+    if st != 0:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv
 
 
 def kernel_name(q, k, v, causal: bool = False, scale: Optional[float] = None) -> str:

@@ -9,6 +9,7 @@
 #include <limits>
 
 #include "attn.h"
+#include "bwd_bf16.h"
 #include "decode.h"
 #include "fwd_bf16.h"
 #include "fwd_f32.h"
@@ -232,6 +233,105 @@ extern "C" attn_status_t attn_fwd_varlen(const attn_fwd_varlen_args_t* a, void* 
     case 64: return c ? launch_fwd_bf16<64, true>(p, grid_x, s) : launch_fwd_bf16<64, false>(p, grid_x, s);
     case 80: return c ? launch_fwd_bf16<80, true>(p, grid_x, s) : launch_fwd_bf16<80, false>(p, grid_x, s);
     case 128: return c ? launch_fwd_bf16<128, true>(p, grid_x, s) : launch_fwd_bf16<128, false>(p, grid_x, s);
+  }
+  return ATTN_ERR_UNSUPPORTED;
+}
+
+// ------------------------------------------------------------------ backward
+bool bwd_head_dim_supported(int64_t d) { return d == 64 || d == 128; }
+
+extern "C" size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq) {
+  if (B < 0 || Hq < 0 || Lq < 0) return 0;
+  return (size_t)((B * Hq * Lq * 4 + 255) / 256 * 256);
+}
+
+extern "C" attn_status_t attn_validate_bwd(const attn_bwd_args_t* a) {
+  if (!a) return ATTN_ERR_NULL;
+  if (a->dtype != ATTN_BF16 && a->dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+  if (a->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (a->B < 0 || a->Hq < 0 || a->Hkv < 0 || a->Lq < 0 || a->Lk < 0 || a->d < 0) return ATTN_ERR_SHAPE;
+  if (!std::isfinite(a->scale)) return ATTN_ERR_SHAPE;
+  if (!bwd_head_dim_supported(a->d)) return ATTN_ERR_UNSUPPORTED;
+  if (a->Hq > 0 && (a->Hkv == 0 || a->Hq % a->Hkv != 0)) return ATTN_ERR_SHAPE;
+  const bool work = a->B > 0 && a->Hq > 0 && (a->Lq > 0 || a->Lk > 0);
+  if (!work) return ATTN_OK;
+  if (a->Lq > 0 && (!a->q || !a->o || !a->dout || !a->lse || !a->dq)) return ATTN_ERR_NULL;
+  if (a->Lk > 0 && (!a->k || !a->v || !a->dk || !a->dv)) return ATTN_ERR_NULL;
+  if (a->Lq > 0 && (!aligned16(a->q) || !aligned16(a->o) || !aligned16(a->dout) || !aligned16(a->dq) ||
+                    (reinterpret_cast<uintptr_t>(a->lse) & 3u) != 0))
+    return ATTN_ERR_LAYOUT;
+  if (a->Lk > 0 && (!aligned16(a->k) || !aligned16(a->v) || !aligned16(a->dk) || !aligned16(a->dv)))
+    return ATTN_ERR_LAYOUT;
+  const int64_t* st[] = {a->q_strides, a->k_strides, a->v_strides, a->o_strides,
+                         a->do_strides, a->dq_strides, a->dk_strides, a->dv_strides};
+  for (const int64_t* x : st)
+    if (!strides_ok(x, 3, 2)) return ATTN_ERR_LAYOUT;
+  if (a->Lq > kI32Max || a->Lk > kI32Max || a->B * a->Hq > kI32Max || a->B * a->Hq * a->Lq > kI32Max * 64)
+    return ATTN_ERR_UNSUPPORTED;
+  if (a->B * a->Hkv * ((a->Lk + 127) / 128) > kI32Max || a->B * a->Hq * ((a->Lq + 127) / 128) > kI32Max)
+    return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+template <int D>
+static attn_status_t launch_bwd(const BwdParams& p, bool causal, hipStream_t s) {
+  const int64_t rows = (int64_t)p.B * p.Hq * p.Lq;
+  if (rows > 0) {
+    hipLaunchKernelGGL(attn_bwd_delta_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, p);
+    if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
+  }
+  const int g_kv = p.B * p.Hkv * ((p.Lk + 127) / 128);
+  if (g_kv > 0) {
+    if (causal)
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true>), dim3(g_kv), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false>), dim3(g_kv), dim3(256), 0, s, p);
+    if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
+  }
+  const int g_q = p.B * p.Hq * ((p.Lq + 127) / 128);
+  if (g_q > 0) {
+    if (causal)
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<D, true>), dim3(g_q), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<D, false>), dim3(g_q), dim3(256), 0, s, p);
+    if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+extern "C" attn_status_t attn_bwd(const attn_bwd_args_t* a, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  const attn_status_t st = attn_validate_bwd(a);
+  if (st != ATTN_OK) return st;
+  if (a->B == 0 || a->Hq == 0 || (a->Lq == 0 && a->Lk == 0)) return ATTN_OK;
+  const size_t need = attn_bwd_workspace_bytes(a->B, a->Hq, a->Lq);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_LAYOUT;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  BwdParams p;
+  p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->o; p.dout = a->dout; p.lse = a->lse;
+  p.delta = reinterpret_cast<float*>(workspace);
+  p.dq = a->dq; p.dk = a->dk; p.dv = a->dv;
+  p.q_sb = a->q_strides[0]; p.q_sh = a->q_strides[1]; p.q_st = a->q_strides[2];
+  p.k_sb = a->k_strides[0]; p.k_sh = a->k_strides[1]; p.k_st = a->k_strides[2];
+  p.v_sb = a->v_strides[0]; p.v_sh = a->v_strides[1]; p.v_st = a->v_strides[2];
+  p.o_sb = a->o_strides[0]; p.o_sh = a->o_strides[1]; p.o_st = a->o_strides[2];
+  p.do_sb = a->do_strides[0]; p.do_sh = a->do_strides[1]; p.do_st = a->do_strides[2];
+  p.dq_sb = a->dq_strides[0]; p.dq_sh = a->dq_strides[1]; p.dq_st = a->dq_strides[2];
+  p.dk_sb = a->dk_strides[0]; p.dk_sh = a->dk_strides[1]; p.dk_st = a->dk_strides[2];
+  p.dv_sb = a->dv_strides[0]; p.dv_sh = a->dv_strides[1]; p.dv_st = a->dv_strides[2];
+  p.B = (int)a->B;
+  p.Hq = (int)a->Hq;
+  p.Hkv = (int)a->Hkv;
+  p.group = (int)(a->Hq / a->Hkv);
+  p.Lq = (int)a->Lq;
+  p.Lk = (int)a->Lk;
+  p.scale = effective_scale(a->scale, a->d);
+  p.scale_log2 = p.scale * kLog2e;
+  const bool c = a->causal != 0;
+  switch (a->d) {
+    case 64: return launch_bwd<64>(p, c, s);
+    case 128: return launch_bwd<128>(p, c, s);
   }
   return ATTN_ERR_UNSUPPORTED;
 }

@@ -251,3 +251,57 @@ def test_varlen_empty_is_noop():
     # no keys at all: k and v may be NULL (every row gets O = 0, LSE = -inf)
     assert vvar(total_k=0, k=0, v=0) == OK
     assert L.attn_validate_fwd_varlen(None) == NULL
+
+
+def bwd_args(**kw):
+    a = sdpa.BwdArgs()
+    B, Hq, Hkv, Lq, Lk, d = (kw.get("B", 2), kw.get("Hq", 8), kw.get("Hkv", 2), kw.get("Lq", 300),
+                             kw.get("Lk", 300), kw.get("d", 64))
+    names = ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv")
+    for i, n in enumerate(names):
+        setattr(a, n, kw.get(n, P + i * 0x10000000))
+    a.B, a.Hq, a.Hkv, a.Lq, a.Lk, a.d = B, Hq, Hkv, Lq, Lk, d
+    qs, ks = (Hq * Lq * d, Lq * d, d), (Hkv * Lk * d, Lk * d, d)
+    for n, dflt in (("q", qs), ("k", ks), ("v", ks), ("o", qs), ("do", qs), ("dq", qs), ("dk", ks), ("dv", ks)):
+        setattr(a, f"{n}_strides", sdpa._i64x3(*kw.get(f"{n}s", dflt)))
+    a.dtype = kw.get("dtype", sdpa.ATTN_BF16)
+    a.causal = kw.get("causal", 0)
+    a.scale = kw.get("scale", 0.0)
+    return a
+
+
+def vbwd(**kw):
+    return sdpa.lib().attn_validate_bwd(ctypes.byref(bwd_args(**kw)))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("Lq,Lk", [(300, 300), (100, 700), (700, 100)])
+def test_bwd_valid(d, causal, Lq, Lk):
+    assert vbwd(d=d, causal=causal, Lq=Lq, Lk=Lk) == OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), NULL), (dict(dout=0), NULL), (dict(lse=0), NULL), (dict(dq=0), NULL), (dict(dk=0), NULL),
+    (dict(dv=0), NULL), (dict(dtype=1), UNSUP), (dict(dtype=9), DTYPE), (dict(d=80), UNSUP), (dict(d=96), UNSUP),
+    (dict(Hkv=3), SHAPE), (dict(Lq=-1), SHAPE), (dict(scale=float("nan")), SHAPE),
+    (dict(dq=P + 8), LAYOUT), (dict(lse=P + 2), LAYOUT), (dict(dos=(8 * 300 * 64, 300 * 64, 66)), LAYOUT),
+])
+def test_bwd_rejections(kw, status):
+    assert vbwd(**kw) == status
+    ws = sdpa.attn_bwd_workspace_bytes(2, 8, 300)
+    assert sdpa.lib().attn_bwd(ctypes.byref(bwd_args(**kw)), P, ws, None) == status
+
+
+def test_bwd_workspace_rules():
+    L = sdpa.lib()
+    need = sdpa.attn_bwd_workspace_bytes(2, 8, 300)
+    assert need == (2 * 8 * 300 * 4 + 255) // 256 * 256
+    assert L.attn_bwd(ctypes.byref(bwd_args()), None, need, None) == WS
+    assert L.attn_bwd(ctypes.byref(bwd_args()), P, need - 1, None) == WS
+    assert L.attn_bwd(ctypes.byref(bwd_args()), P + 16, need, None) == LAYOUT
+    assert sdpa.attn_bwd_workspace_bytes(-1, 8, 3) == 0
+    # nothing to do: no call touches the device
+    assert L.attn_bwd(ctypes.byref(bwd_args(B=0)), None, 0, None) == OK
+    assert L.attn_bwd(ctypes.byref(bwd_args(Lq=0, Lk=0)), None, 0, None) == OK
+    assert L.attn_validate_bwd(None) == NULL

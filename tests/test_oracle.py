@@ -478,6 +478,17 @@ def test_planted_mistakes(monkeypatch, kind):
     assert failures >= 1, f"planted mistake {kind} not caught"
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_sampled_is_the_same_definition(causal):
+    q, k, v = rnd((2, 4, 23, 8), 133), rnd((2, 2, 23, 8), 134), rnd((2, 2, 23, 8), 135)
+    do = rnd((2, 4, 23, 8), 136)
+    dq, dk, dv = orc.attention_backward(q, k, v, do, causal=causal)
+    rows, keys = [0, 9, 22], [1, 11, 22]
+    sq, sk, sv = orc.attention_backward_sampled(q, k, v, do, 1, 1, rows, keys, causal=causal)
+    assert np.abs(sq - dq[1, 2:4][:, rows]).max() <= 1e-12
+    assert np.abs(sk - dk[1, 1, keys]).max() <= 1e-12 and np.abs(sv - dv[1, 1, keys]).max() <= 1e-12
+
+
 def _backward_mutant(kind):
     """Copies of the oracle's per-head backward with one plausible slip each."""
     def f(q, k, v, do, scale, causal):

@@ -1,0 +1,136 @@
+"""Backward parity: the HIP attn_bwd against the float64 CPU oracle.
+
+The GPU forward supplies O and LSE exactly as a caller's would; the oracle's
+gradients come from the bf16 input values widened to float64.  Small and
+medium shapes are compared in full; the causal GQA n=8192 d=128 workload at
+its real size on sampled query rows and keys.  Gate per gradient tensor: the
+stated bf16 tolerance (max-abs <= 2e-2, mean-abs <= 1e-3) applied to the
+tensor divided by s = max(1, max |reference|).  Gradients, unlike O, are not
+bounded by the values' range (a kv head's dV sums the output gradients of its
+query rows and heads), and rounding a result to bf16 alone moves it by up to
+2^-9 of its magnitude; dividing by s keeps the stated bound wherever values
+stay within +-1 and makes it relative where they are larger.
+"""
+import numpy as np
+import pytest
+import torch
+
+import scaled_dot_product_qk_amd as sdpa
+import workloads as wl
+from oracle import sdpa_oracle as orc
+from parity_util import BF16_MAX_ABS, BF16_MEAN_ABS, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU parity tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def grad_check(name, got, ref, label):
+    got = np.asarray(got, np.float64)
+    d = np.abs(got - ref)
+    e = dict(max_abs=float(d.max()) if d.size else 0.0, mean_abs=float(d.mean()) if d.size else 0.0,
+             ref_max=float(np.abs(ref).max()) if ref.size else 0.0)
+    print(f"[parity] {label} {name}: " + " ".join(f"{k}={v:.3e}" for k, v in e.items()), flush=True)
+    assert np.isfinite(got).all(), f"non-finite values in {name}"
+    sc = max(1.0, e["ref_max"])
+    assert e["max_abs"] <= BF16_MAX_ABS * sc, (name, e)
+    assert e["mean_abs"] <= BF16_MEAN_ABS * sc, (name, e)
+
+
+def inputs(w, seed_do):
+    q, k, v = wl.make_fwd_inputs(w)
+    g = torch.Generator().manual_seed(seed_do)
+    do = torch.randn(q.shape, generator=g, dtype=torch.float32).to(q.dtype)
+    return q, k, v, do
+
+
+def run_gpu(q, k, v, do, dev, causal):
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    o, lse = sdpa.attn_fwd(qd, kd, vd, causal=causal)
+    dq, dk, dv = sdpa.attn_bwd(qd, kd, vd, o, lse, dod, causal=causal)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+SHAPES = [
+    # (B, Hq, Hkv, Lq, Lk)
+    (2, 4, 2, 300, 300),   # ragged: query and key tiles of 128 with a 44-row tail
+    (1, 2, 1, 1, 1),
+    (1, 4, 4, 129, 129),
+    (2, 8, 1, 257, 257),   # multi-query: dK, dV summed over 8 heads
+    (2, 4, 2, 77, 500),    # cross-attention lengths
+    (1, 4, 2, 500, 77),
+]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_bwd_small(dev, d, causal, shape):
+    B, Hq, Hkv, Lq, Lk = shape
+    w = wl.FwdWorkload("bwd", B, Hq, Hkv, Lq, Lk, d, "bf16", causal, 900 + Lq + Lk + d)
+    q, k, v, do = inputs(w, 950 + d)
+    dq, dk, dv = run_gpu(q, k, v, do, dev, causal)
+    rq, rk, rv = orc.attention_backward(q, k, v, do, causal=causal)
+    label = f"bwd d{d} causal={causal} {shape}"
+    grad_check("dq", to_np(dq), rq, label)
+    grad_check("dk", to_np(dk), rk, label)
+    grad_check("dv", to_np(dv), rv, label)
+
+
+def test_bwd_deterministic(dev):
+    w = wl.FwdWorkload("bwd_det", 1, 8, 2, 700, 700, 128, "bf16", True, 960)
+    q, k, v, do = inputs(w, 961)
+    a = run_gpu(q, k, v, do, dev, True)
+    b = run_gpu(q, k, v, do, dev, True)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_bwd_no_queries_gives_zero_key_gradients(dev):
+    q = torch.zeros(1, 2, 0, 64, dtype=torch.bfloat16, device=dev)
+    k = torch.randn(1, 2, 100, 64, device=dev).to(torch.bfloat16)
+    v = torch.randn(1, 2, 100, 64, device=dev).to(torch.bfloat16)
+    lse = torch.zeros(1, 2, 0, device=dev)
+    dk = torch.full_like(k, 7.0)
+    dv = torch.full_like(v, 7.0)
+    sdpa.attn_bwd(q, k, v, q, lse, q, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert (dk == 0).all() and (dv == 0).all()
+
+
+def test_bwd_strided_layout(dev):
+    """[B, L, H, d] tensors viewed as [B, H, L, d] (token stride H*d)."""
+    B, H, L, d = 2, 4, 200, 64
+    w = wl.FwdWorkload("bwd_strided", B, H, H, L, L, d, "bf16", False, 970)
+    q, k, v, do = inputs(w, 971)
+    rq, rk, rv = orc.attention_backward(q, k, v, do)
+    t = [x.transpose(1, 2).contiguous().to(dev).transpose(1, 2) for x in (q, k, v, do)]
+    o, lse = sdpa.attn_fwd(t[0], t[1], t[2])
+    dq, dk, dv = sdpa.attn_bwd(t[0], t[1], t[2], o, lse, t[3])
+    torch.cuda.synchronize()
+    grad_check("dq", to_np(dq), rq, "bwd strided")
+    grad_check("dk", to_np(dk), rk, "bwd strided")
+    grad_check("dv", to_np(dv), rv, "bwd strided")
+
+
+def test_workload_bwd_causal_gqa_n8192_sampled(dev):
+    """The causal GQA n=8192 d=128 workload at full size, as the benchmark
+    runs it; sampled query rows (every head of kv group 0 and 7) and sampled
+    keys against the oracle's per-head evaluation."""
+    w = wl.C4
+    q, k, v, do = inputs(w, wl.C4.seed + 50)
+    dq, dk, dv = run_gpu(q, k, v, do, dev, True)
+    dq, dk, dv = to_np(dq), to_np(dk), to_np(dv)
+    rows = [0, 1, 127, 128, 4095, 8191]
+    keys = [0, 63, 64, 4096, 8190, 8191]
+    g = w.Hq // w.Hkv
+    for hk in (0, w.Hkv - 1):
+        sq, sk, sv = orc.attention_backward_sampled(q, k, v, do, 0, hk, rows, keys, causal=True)
+        grad_check("dq", dq[0, hk * g:(hk + 1) * g][:, rows], sq, f"C4 bwd kv head {hk}")
+        grad_check("dk", dk[0, hk, keys], sk, f"C4 bwd kv head {hk}")
+        grad_check("dv", dv[0, hk, keys], sv, f"C4 bwd kv head {hk}")

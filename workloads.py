@@ -185,6 +185,19 @@ def algorithmic_bytes_fwd(B, Hq, Hkv, Lq, Lk, d, elem_bytes) -> int:
     return (B * Hq * Lq * d * 2 + B * Hkv * Lk * d * 2) * elem_bytes + B * Hq * Lq * 4
 
 
+def algorithmic_flops_bwd(B, Hq, Lq, Lk, d, causal) -> int:
+    """The backward's five products (Q K^T recomputed, dP = dO V^T, dV = P^T dO,
+    dQ = dS K, dK = dS^T Q), 2 Lq Lk d flops each per (batch, query head):
+    2.5 times the forward's count; causal credited as exactly half."""
+    f = 10 * B * Hq * Lq * Lk * d
+    return f // 2 if causal else f
+
+
+def algorithmic_bytes_bwd(B, Hq, Hkv, Lq, Lk, d, elem_bytes) -> int:
+    """Q, K, V, O, dO and LSE read once; dQ, dK, dV written once."""
+    return (3 * B * Hq * Lq * d + 4 * B * Hkv * Lk * d) * elem_bytes + B * Hq * Lq * 4
+
+
 def algorithmic_flops_varlen(lens_q, lens_k, Hq, d, causal) -> int:
     """Sum over sequences of the dense count; causal credited as exactly half."""
     return sum(algorithmic_flops_fwd(1, Hq, int(a), int(b), d, causal) for a, b in zip(lens_q, lens_k))
