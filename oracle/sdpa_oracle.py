@@ -63,12 +63,14 @@ def default_scale(d: int) -> float:
 
 def _head_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
                     causal: bool, row_ids: Optional[np.ndarray] = None,
-                    n_keys: Optional[int] = None, return_sp: bool = False):
+                    n_keys: Optional[int] = None, return_sp: bool = False,
+                    mask: Optional[np.ndarray] = None):
     """One (batch, head) pair: q [n_rows, d], k and v [Lk, d].
 
     row_ids are the absolute query positions of the rows of q (needed for the
     causal mask when only some rows are asked for).  n_keys limits the keys to
-    the first n_keys rows of k and v (decode lengths).
+    the first n_keys rows of k and v (decode lengths).  mask [n_rows, Lk] is a
+    boolean (True: the pair takes part) or an additive float mask.
     """
     if n_keys is not None:
         k = k[:n_keys]
@@ -81,8 +83,12 @@ def _head_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
         if return_sp:
             return o, lse, np.zeros((n_rows, 0)), np.zeros((n_rows, 0))
         return o, lse
-    # Step 1: scores, materialised, then scaled.
+    # Step 1: scores, materialised, then scaled; an additive mask is added to
+    # the scaled scores, a boolean one removes the pairs it marks False.
     s = (q @ k.T) * scale
+    if mask is not None:
+        mask = np.asarray(mask)[:, :lk]
+        s = np.where(mask, s, -np.inf) if mask.dtype == bool else s + mask.astype(np.float64)
     # Step 2: causal mask.
     if causal:
         if row_ids is None:
@@ -116,6 +122,13 @@ def _as64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
+def _as_mask(m) -> np.ndarray:
+    """A boolean mask stays boolean; any other mask is widened to float64."""
+    if str(getattr(m, "dtype", "")) in ("torch.bool", "bool"):
+        return np.asarray(m.numpy() if hasattr(m, "numpy") else m, dtype=bool)
+    return _as64(m)
+
+
 def _pool_map(fn, items: Sequence, threads: Optional[int]):
     if threads is None:
         threads = min(len(items), os.cpu_count() or 1)
@@ -133,11 +146,13 @@ def _pool_map(fn, items: Sequence, threads: Optional[int]):
 
 
 def attention_forward(q, k, v, causal: bool = False, scale: Optional[float] = None,
-                      threads: Optional[int] = None, return_sp: bool = False):
+                      threads: Optional[int] = None, return_sp: bool = False, attn_mask=None):
     """Prefill attention. q [B,Hq,Lq,d]; k, v [B,Hkv,Lk,d] -> O [B,Hq,Lq,d], LSE [B,Hq,Lq].
 
-    With return_sp the materialised S and P [B,Hq,Lq,Lk] are returned as well
-    (small shapes only).
+    attn_mask, broadcastable to [B,Hq,Lq,Lk]: boolean (True: the pair takes
+    part) or additive (added to the scaled scores), as the pages' SDPA call
+    takes it; it combines with causal.  With return_sp the materialised S and
+    P [B,Hq,Lq,Lk] are returned as well (small shapes only).
     """
     q, k, v = _as64(q), _as64(k), _as64(v)
     B, Hq, Lq, d = q.shape
@@ -155,11 +170,15 @@ def attention_forward(q, k, v, causal: bool = False, scale: Optional[float] = No
     p_all = np.zeros((B, Hq, Lq, Lk)) if return_sp else None
     items = [(b, h) for b in range(B) for h in range(Hq)]
 
+    if attn_mask is not None:
+        attn_mask = np.broadcast_to(_as_mask(attn_mask), (B, Hq, Lq, Lk))
+
     def one(item):
         b, h = item
         hk = h // group
         return _head_attention(q[b, h], k[b, hk], v[b, hk], scale, causal,
-                               return_sp=return_sp)
+                               return_sp=return_sp,
+                               mask=None if attn_mask is None else attn_mask[b, h])
 
     results = _pool_map(one, items, threads)
     for (b, h), res in zip(items, results):
@@ -293,7 +312,7 @@ def attention_forward_varlen(q, k, v, cu_q: Sequence[int], cu_k: Sequence[int], 
 
 
 def attention_forward_rows(q, k, v, b: int, h: int, rows: Iterable[int],
-                           causal: bool = False, scale: Optional[float] = None):
+                           causal: bool = False, scale: Optional[float] = None, attn_mask=None):
     """The same definition for a few query rows of one (batch, query head).
 
     Used to check full-size runs on sampled outputs: each row needs only its
@@ -306,8 +325,11 @@ def attention_forward_rows(q, k, v, b: int, h: int, rows: Iterable[int],
     rows = np.asarray(list(rows), dtype=np.int64)
     if scale is None:
         scale = default_scale(q.shape[-1])
+    m = None
+    if attn_mask is not None:
+        m = np.broadcast_to(_as_mask(attn_mask), (q.shape[0], q.shape[1], q.shape[2], k.shape[2]))[b, h][rows]
     return _head_attention(q_bh[rows], _as64(k[b, hk]), _as64(v[b, hk]), scale,
-                           causal, row_ids=rows)
+                           causal, row_ids=rows, mask=m)
 
 
 def attention_decode(q, k_cache, v_cache, seqlens, scale: Optional[float] = None,
@@ -395,11 +417,13 @@ def softmax_two_blocks(x: np.ndarray):
 
 
 def brute_force_attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
-                          n_keys: Optional[Sequence[int]] = None):
+                          n_keys: Optional[Sequence[int]] = None, mask=None):
     """Per-element pure-Python evaluation for tiny shapes (no numpy arithmetic).
 
     q [B][Hq][Lq][d], k and v [B][Hkv][Lk][d] as nested sequences; n_keys
-    optionally limits the keys seen by batch b (decode lengths).  Every score
+    optionally limits the keys seen by batch b (decode lengths); mask
+    [B][Hq][Lq][Lk] of booleans (False removes the pair) or numbers (added to
+    the scaled score).  Every score
     is a math.fsum of products; every row is normalised with math.fsum.
     Returns nested lists O [B][Hq][Lq][d] and LSE [B][Hq][Lq].
     """
@@ -420,12 +444,19 @@ def brute_force_attention(q, k, v, causal: bool = False, scale: Optional[float] 
             Oh, Lh = [], []
             for i, qi in enumerate(q[b][h]):
                 visible = [j for j in range(nk) if not (causal and j > i)]
+                add = {}
+                if mask is not None:
+                    mrow = mask[b][h][i]
+                    if isinstance(mrow[0], (bool, np.bool_)):
+                        visible = [j for j in visible if mrow[j]]
+                    else:
+                        add = {j: float(mrow[j]) for j in visible}
                 if not visible:
                     Oh.append([0.0] * len(vals[0]) if vals else [])
                     Lh.append(-math.inf)
                     continue
                 s = {j: math.fsum(float(qi[t]) * float(keys[j][t]) for t in range(d)) * scale
-                     for j in visible}
+                     + add.get(j, 0.0) for j in visible}
                 m = max(s.values())
                 e = {j: math.exp(s[j] - m) for j in visible}
                 l = math.fsum(e.values())

@@ -373,6 +373,64 @@ def test_varlen_single_sequence_is_dense():
     assert np.array_equal(ov, o[0].transpose(1, 0, 2)) and np.array_equal(lv, lse[0])
 
 
+# ---------------------------------------------------- P-17 attention masks
+def _masks(shape, seed):
+    r = np.random.default_rng(seed)
+    bm = r.random(shape) < 0.7
+    bm[..., 0] = True                      # every row keeps a key (torch gives NaN otherwise)
+    am = r.standard_normal(shape) * 2.0
+    return bm, am
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("kind", ["bool", "add"])
+def test_mask_matches_brute_force(causal, kind):
+    q, k, v = rnd((1, 2, 6, 4), 140, 2.0), rnd((1, 2, 8, 4), 141), rnd((1, 2, 8, 4), 142)
+    bm, am = _masks((1, 2, 6, 8), 143)
+    m = bm if kind == "bool" else am
+    o, lse = orc.attention_forward(q, k, v, causal=causal, attn_mask=m)
+    ob, lb = orc.brute_force_attention(q.tolist(), k.tolist(), v.tolist(), causal=causal, mask=m.tolist())
+    assert np.abs(o - np.array(ob)).max() <= 1e-12 and np.abs(lse - np.array(lb)).max() <= 1e-12
+
+
+@pytest.mark.parametrize("kind", ["bool", "add"])
+def test_mask_matches_torch_sdpa_float64(kind):
+    q, k, v = rnd((2, 4, 19, 16), 144, 2.0), rnd((2, 4, 27, 16), 145), rnd((2, 4, 27, 16), 146)
+    bm, am = _masks((2, 1, 19, 27), 147)          # broadcast over heads
+    m = bm if kind == "bool" else am
+    o, _ = orc.attention_forward(q, k, v, attn_mask=m)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=torch.from_numpy(m)).numpy()
+    assert np.abs(o - ref).max() <= 1e-12
+
+
+def test_mask_closed_forms():
+    q, k, v = rnd((1, 2, 9, 8), 148), rnd((1, 2, 9, 8), 149), rnd((1, 2, 9, 8), 150)
+    o, lse = orc.attention_forward(q, k, v, causal=True)
+    # all-True boolean mask = no mask
+    o1, l1 = orc.attention_forward(q, k, v, causal=True, attn_mask=np.ones((9, 9), bool))
+    assert np.array_equal(o1, o) and np.array_equal(l1, lse)
+    # a constant per row added to every score leaves O and shifts LSE by that constant
+    c = rnd((9, 1), 151)
+    o2, l2 = orc.attention_forward(q, k, v, causal=True, attn_mask=np.broadcast_to(c, (9, 9)))
+    assert np.abs(o2 - o).max() <= 1e-12 and np.abs(l2 - (lse + c[:, 0])).max() <= 1e-12
+    # a boolean mask that keeps only key 0 makes every row return V[0]
+    m = np.zeros((9, 9), bool)
+    m[:, 0] = True
+    o3, _ = orc.attention_forward(q, k, v, attn_mask=m)
+    assert np.abs(o3 - v[:, :, :1]).max() <= 1e-15
+
+
+def test_fully_masked_row_gives_zero_and_minus_inf():
+    q, k, v = rnd((1, 1, 4, 4), 152), rnd((1, 1, 5, 4), 153), rnd((1, 1, 5, 4), 154)
+    m = np.ones((4, 5), bool)
+    m[2] = False
+    o, lse = orc.attention_forward(q, k, v, attn_mask=m)
+    assert (o[0, 0, 2] == 0).all() and np.isneginf(lse[0, 0, 2]) and np.isfinite(lse[0, 0, [0, 1, 3]]).all()
+    ob, lb = orc.brute_force_attention(q.tolist(), k.tolist(), v.tolist(), mask=m[None, None].tolist())
+    assert np.abs(o - np.array(ob)).max() <= 1e-12
+
+
 # --------------------------------------------------- P-16 backward pass
 def _loss(q, k, v, w, causal):
     o, _ = orc.attention_forward(q, k, v, causal=causal)
@@ -437,10 +495,12 @@ def test_backward_invariants(causal):
 # -------------------------------------------- planted mistakes are caught
 def _mutant(kind):
     """Copies of the oracle's per-head step with one plausible slip each."""
-    def f(q, k, v, scale, causal, row_ids=None, n_keys=None, return_sp=False):
+    def f(q, k, v, scale, causal, row_ids=None, n_keys=None, return_sp=False, mask=None):
         if kind == "scale_1_over_d":
             scale = scale * scale
         s = (q @ k.T) * scale
+        if mask is not None:
+            s = np.where(mask, s, -np.inf) if np.asarray(mask).dtype == bool else s + mask
         if kind == "transposed" and s.shape[0] == s.shape[1]:
             s = s.T.copy()
         n_rows, lk = s.shape
@@ -470,7 +530,8 @@ def test_planted_mistakes(monkeypatch, kind):
                lambda: test_key_shift_moves_only_lse(True),
                lambda: test_constant_values_return_the_constant(False),
                lambda: test_cross_attention_causal_matches_torch_sdpa_float64(20, 33),
-               lambda: test_varlen_matches_brute_force_per_sequence(3, True)):
+               lambda: test_varlen_matches_brute_force_per_sequence(3, True),
+               lambda: test_mask_matches_torch_sdpa_float64("add")):
         try:
             fn()
         except AssertionError:
