@@ -7,9 +7,10 @@ One step = one pass of the whole path over synthetic, HBM-resident inputs:
 Each call is timed with HIP events recorded on the stream the kernels run on;
 the step as a whole is timed with host clocks between device synchronisations.
 After the step loop, attn_fwd_varlen on 16 packed causal GQA sequences of
-256..4096 tokens (d=128) and attn_bwd on the causal GQA n=8192 d=128 workload
-are timed the same way, each on its own, and reported in `extra` (they are not
-part of the step).
+256..4096 tokens (d=128), attn_bwd on the causal GQA n=8192 d=128 workload and
+attn_fwd_masked on the n=4096 d=64 workload with one boolean mask shared by
+all heads are timed the same way, each on its own, and reported in `extra`
+(they are not part of the step).
 
 Prints ONE JSON line.  `value` is the headline workload's attention-forward
 throughput in TFLOP/s (credited flops 4 n^2 d H B, halved when causal).
@@ -72,7 +73,8 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "fwd_n4096", "fwd_causal_n8192", "decode", "fwd_varlen", "bwd"],
+    ap.add_argument("--only", choices=["all", "fwd_n4096", "fwd_causal_n8192", "decode", "fwd_varlen", "bwd",
+                                       "fwd_masked"],
                     default="all",
                     help="time one call of the step only (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -127,10 +129,12 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     names = ["fwd_n4096", "fwd_causal_n8192", "decode"] if args.only == "all" else \
-        ([] if args.only in ("fwd_varlen", "bwd") else [args.only])
+        ([] if args.only in ("fwd_varlen", "bwd", "fwd_masked") else [args.only])
     with_varlen = args.only in ("all", "fwd_varlen")
     with_bwd = args.only in ("all", "bwd")
-    solo = (["fwd_varlen"] if with_varlen else []) + (["bwd"] if with_bwd else [])
+    with_masked = args.only in ("all", "fwd_masked")
+    solo = (["fwd_varlen"] if with_varlen else []) + (["bwd"] if with_bwd else []) + \
+        (["fwd_masked"] if with_masked else [])
 
     # ---- inputs, generated on the host and copied once to HBM ----
     calls = {}
@@ -175,6 +179,14 @@ def main():
         wsb = torch.empty(sdpa.attn_bwd_workspace_bytes(wl.C4.B, wl.C4.Hq, wl.C4.Lq), dtype=torch.uint8, device=dev)
         calls["bwd"] = lambda: sdpa.attn_bwd(GB[0], GB[1], GB[2], ob, lb, GB[3], causal=True, dq=dqb, dk=dkb,
                                              dv=dvb, workspace=wsb, stream=stream)
+    if with_masked:
+        qm, km, vm = wl.make_fwd_inputs(wl.C2)
+        GM = [t.to(dev) for t in (qm, km, vm)]
+        del qm, km, vm
+        mm = wl.make_mask((1, 1, wl.C2.Lq, wl.C2.Lk), "bool", 1007).to(dev)
+        om = torch.empty_like(GM[0])
+        lm = torch.empty(GM[0].shape[:3], dtype=torch.float32, device=dev)
+        calls["fwd_masked"] = lambda: sdpa.attn_fwd_masked(*GM, mm, out=om, lse=lm, stream=stream)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -244,6 +256,13 @@ def main():
                       "algorithmic_flops": fb,
                       "algorithmic_bytes": wl.algorithmic_bytes_bwd(C4.B, C4.Hq, C4.Hkv, C4.Lq, C4.Lk, C4.d, 2)}
 
+    if "fwd_masked" in ms:
+        t = ms["fwd_masked"] / 1e3
+        res["fwd_masked"] = {"kernel": "attn_fwd_bf16_kernel<64, false, 1> (boolean mask, shared by all heads)",
+                             "ms": ms["fwd_masked"], "tflops": f2 / t / 1e12, "algorithmic_flops": f2,
+                             "algorithmic_bytes": wl.algorithmic_bytes_fwd(C2.B, C2.Hq, C2.Hkv, C2.Lq, C2.Lk, C2.d, 2)
+                             + C2.Lq * C2.Lk}
+
     def roof_fwd(r, tag):
         tr = counted_traffic(tag)
         return {"bound": "mfma", "achieved": r["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -279,6 +298,9 @@ def main():
     if "fwd_varlen" in res:
         r = res["fwd_varlen"]
         out["extra"]["fwd_varlen_causal_gqa_b16_d128"] = dict(r, roofline=roof_fwd(r, "attn_fwd_varlen_d128_causal_b16"))
+    if "fwd_masked" in res:
+        r = res["fwd_masked"]
+        out["extra"]["fwd_masked_bool_shared_n4096_d64"] = dict(r, roofline=roof_fwd(r, "attn_fwd_masked_d64_n4096"))
     if "bwd" in res:
         r = res["bwd"]
         out["extra"]["bwd_causal_gqa_n8192_d128"] = dict(r, roofline=roof_fwd(r, "attn_bwd_d128_causal_n8192"))

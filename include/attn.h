@@ -95,7 +95,22 @@ typedef struct {
   float scale;     /* multiplier of Q K^T; 0 selects 1/sqrt(d) */
 } attn_fwd_args_t;
 
-/* Packed variable-length prefill ("Flash Attention原理：分块计算与重计算"
+/* Attention mask for attn_fwd_masked ("Flash Attention原理：分块计算与重计算"
+ * (cnblogs), FAQ Q11: any boolean mask, applied inside the kernel; the
+ * semantics of scaled_dot_product_attention's attn_mask). */
+typedef enum {
+  ATTN_MASK_BOOL = 1,      /* uint8: nonzero = the (query, key) pair takes part */
+  ATTN_MASK_ADD_BF16 = 2   /* bf16, added to the scaled score before the softmax */
+} attn_mask_kind_t;
+
+typedef struct {
+  const void *data;     /* [B, Hq, Lq, Lk] logical shape, key-contiguous */
+  int32_t kind;         /* attn_mask_kind_t */
+  int32_t reserved;     /* 0 */
+  int64_t strides[3];   /* element strides of (batch, head, query); 0 broadcasts */
+} attn_mask_t;
+
+/* Packed variable-length prefill ("Flash Attention原理：分块计算与重计算"/* Packed variable-length prefill ("Flash Attention原理：分块计算与重计算"
  * (cnblogs), FAQ Q10: several sequences of different lengths packed into one
  * batch through cumulative sequence offsets, no padding; FAQ Q15: queries and
  * keys/values of different lengths, as in cross-attention).  Sequence b owns
@@ -178,6 +193,19 @@ typedef struct {
 attn_status_t attn_fwd(const attn_fwd_args_t *args, void *stream);
 
 /*
+ * attn_fwd_masked - attn_fwd with an attention mask, one kernel launch.  The
+ * mask combines with causal (a pair takes part only if both allow it); a row
+ * left without any key gets O = 0 and LSE = -inf.  Supported: dtype bf16;
+ * d in {64, 80, 128}; the mask's data 16-byte aligned, its query stride a
+ * multiple of 16 bytes and below 2^27 bytes, Lk a multiple of 16 (boolean)
+ * or 8 (additive) keys.  The mask tile of every key tile is read from device
+ * memory: a mask with its own values per head adds Lq x Lk elements per head
+ * to the traffic (strides 0 share one mask between heads or batches).
+ */
+attn_status_t attn_fwd_masked(const attn_fwd_args_t *args, const attn_mask_t *mask, void *stream);
+
+/*
+ * attn_fwd_varlen - packed variable-length prefill, one kernel launch: the/*
  * attn_fwd_varlen - packed variable-length prefill, one kernel launch: the
  * same computation as attn_fwd applied to each sequence separately.
  * Supported: dtype bf16; d in {64, 80, 128}; Hq % Hkv == 0;
@@ -241,6 +269,7 @@ attn_status_t attn_bwd(const attn_bwd_args_t *args, void *workspace, size_t work
  * attn_decode would return before launching.  Usable without a GPU. *//* Argument checks only (no device work, no HIP call): the status attn_fwd /
  * attn_decode would return before launching.  Usable without a GPU. */
 attn_status_t attn_validate_fwd(const attn_fwd_args_t *args);
+attn_status_t attn_validate_fwd_masked(const attn_fwd_args_t *args, const attn_mask_t *mask);
 attn_status_t attn_validate_fwd_varlen(const attn_fwd_varlen_args_t *args);
 attn_status_t attn_validate_bwd(const attn_bwd_args_t *args);
 attn_status_t attn_validate_decode(const attn_decode_args_t *args);

@@ -20,10 +20,11 @@ ATTN_BF16, ATTN_F32 = 0, 1
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_DTYPE",
                 4: "ATTN_ERR_LAYOUT", 5: "ATTN_ERR_UNSUPPORTED", 6: "ATTN_ERR_WORKSPACE",
                 7: "ATTN_ERR_HIP"}
-EXPORTED = ("attn_fwd", "attn_fwd_varlen", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode",
-            "attn_decode_workspace_bytes", "attn_validate_fwd", "attn_validate_fwd_varlen",
-            "attn_validate_bwd", "attn_validate_decode", "attn_status_str", "attn_kernel_name",
-            "attn_version")
+EXPORTED = ("attn_fwd", "attn_fwd_masked", "attn_fwd_varlen", "attn_bwd", "attn_bwd_workspace_bytes",
+            "attn_decode", "attn_decode_workspace_bytes", "attn_validate_fwd", "attn_validate_fwd_masked",
+            "attn_validate_fwd_varlen", "attn_validate_bwd", "attn_validate_decode", "attn_status_str",
+            "attn_kernel_name", "attn_version")
+ATTN_MASK_BOOL, ATTN_MASK_ADD_BF16 = 1, 2
 
 _i64 = ctypes.c_int64
 _i64x3 = _i64 * 3
@@ -37,6 +38,11 @@ class FwdArgs(ctypes.Structure):
                 ("q_strides", _i64x3), ("k_strides", _i64x3), ("v_strides", _i64x3),
                 ("o_strides", _i64x3),
                 ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class MaskArgs(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("kind", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("strides", _i64x3)]
 
 
 class FwdVarlenArgs(ctypes.Structure):
@@ -91,6 +97,10 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd.restype = ctypes.c_int
         L.attn_validate_fwd.argtypes = [ctypes.POINTER(FwdArgs)]
         L.attn_validate_fwd.restype = ctypes.c_int
+        L.attn_fwd_masked.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(MaskArgs), ctypes.c_void_p]
+        L.attn_fwd_masked.restype = ctypes.c_int
+        L.attn_validate_fwd_masked.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(MaskArgs)]
+        L.attn_validate_fwd_masked.restype = ctypes.c_int
         L.attn_fwd_varlen.argtypes = [ctypes.POINTER(FwdVarlenArgs), ctypes.c_void_p]
         L.attn_fwd_varlen.restype = ctypes.c_int
         L.attn_validate_fwd_varlen.argtypes = [ctypes.POINTER(FwdVarlenArgs)]
@@ -198,6 +208,52 @@ def attn_fwd(q, k, v, causal: bool = False, scale: Optional[float] = None, out=N
     st = lib().attn_fwd(ctypes.byref(args), _stream_handle(stream))
     if st != 0:
         raise AttnError(st, "attn_fwd")
+    return out, lse
+
+
+def make_mask_args(mask, B: int, Hq: int, Lq: int, Lk: int) -> MaskArgs:
+    """mask: bool (True = the pair takes part) or bf16 additive, broadcastable to
+    [B, Hq, Lq, Lk] through its batch and head dimensions (4-D, key-contiguous)."""
+    import torch
+    if mask.dim() != 4 or mask.shape[2] != Lq or mask.shape[3] != Lk or mask.shape[0] not in (1, B) \
+            or mask.shape[1] not in (1, Hq):
+        raise ValueError(f"mask must be [B|1, Hq|1, Lq, Lk]; got {tuple(mask.shape)}")
+    if mask.numel() and mask.stride(3) != 1:
+        raise ValueError("the mask's key dimension must be contiguous")
+    m = MaskArgs()
+    m.data = mask.data_ptr()
+    if mask.dtype == torch.bool:
+        m.kind = ATTN_MASK_BOOL
+    elif mask.dtype == torch.bfloat16:
+        m.kind = ATTN_MASK_ADD_BF16
+    else:
+        raise ValueError("mask must be torch.bool or torch.bfloat16 (additive)")
+    sb = 0 if mask.shape[0] == 1 else mask.stride(0)
+    sh = 0 if mask.shape[1] == 1 else mask.stride(1)
+    m.strides = _i64x3(sb, sh, mask.stride(2))
+    return m
+
+
+def attn_fwd_masked(q, k, v, mask, causal: bool = False, scale: Optional[float] = None, out=None, lse=None,
+                    stream=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """attn_fwd with an attention mask (bool: True = take part; bf16: added to
+    the scaled scores), broadcastable over batch and heads."""
+    import torch
+    _check_fwd_tensors(q, k, v)
+    _check_device(q, mask)
+    B, Hq, Lq, d = q.shape
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    _check_device(q, out, lse)
+    if not lse.is_contiguous() or lse.dtype != torch.float32 or lse.shape != (B, Hq, Lq):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Lq] tensor")
+    args = make_fwd_args(q, k, v, out, lse, causal, scale)
+    margs = make_mask_args(mask, B, Hq, Lq, k.shape[2])
+    st = lib().attn_fwd_masked(ctypes.byref(args), ctypes.byref(margs), _stream_handle(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_masked")
     return out, lse
 
 

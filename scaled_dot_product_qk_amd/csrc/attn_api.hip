@@ -92,10 +92,10 @@ static attn_status_t launch_status() {
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int MK = 0>
 static attn_status_t launch_fwd_bf16(const FwdParams& p, int grid_x, hipStream_t s) {
-  constexpr int lds = Bf16FwdShape<D>::kLdsBytes;
-  auto kern = attn_fwd_bf16_kernel<D, CAUSAL>;
+  constexpr int lds = Bf16FwdShape<D>::kLdsBytes + FwdMaskShape<D, MK>::kLdsBytes;
+  auto kern = attn_fwd_bf16_kernel<D, CAUSAL, MK>;
   static bool attr_set = false;  // racing first calls set the same value
   if (!attr_set) {
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=
@@ -124,12 +124,7 @@ static attn_status_t launch_fwd_f32(const FwdParams& p, int grid_x, hipStream_t 
   return launch_status();
 }
 
-extern "C" attn_status_t attn_fwd(const attn_fwd_args_t* a, void* stream) {
-  const attn_status_t st = attn_validate_fwd(a);
-  if (st != ATTN_OK) return st;
-  if (a->B == 0 || a->Hq == 0 || a->Lq == 0) return ATTN_OK;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-
+static FwdParams dense_fwd_params(const attn_fwd_args_t* a) {
   FwdParams p;
   p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->o; p.lse = a->lse;
   p.q_sb = a->q_strides[0]; p.q_sh = a->q_strides[1]; p.q_st = a->q_strides[2];
@@ -147,12 +142,23 @@ extern "C" attn_status_t attn_fwd(const attn_fwd_args_t* a, void* stream) {
   p.cu_q = nullptr;
   p.cu_k = nullptr;
   p.total_q = p.total_k = 0;
+  p.mask = nullptr;
+  p.m_sb = p.m_sh = p.m_sq = 0;
   p.scale_log2 = effective_scale(a->scale, a->d) * kLog2e;
   p.scale_log2_abs = std::fabs(p.scale_log2);
+  p.inv_abs_scale = 1.0f / std::fabs(effective_scale(a->scale, a->d));
   p.neg_q = p.scale_log2 < 0.f ? 1 : 0;
+  return p;
+}
+
+extern "C" attn_status_t attn_fwd(const attn_fwd_args_t* a, void* stream) {
+  const attn_status_t st = attn_validate_fwd(a);
+  if (st != ATTN_OK) return st;
+  if (a->B == 0 || a->Hq == 0 || a->Lq == 0) return ATTN_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const FwdParams p = dense_fwd_params(a);
   const int grid_x = (int)(a->B * a->Hq);
   const bool c = a->causal != 0;
-
   if (a->dtype == ATTN_BF16) {
     switch (a->d) {
       case 64: return c ? launch_fwd_bf16<64, true>(p, grid_x, s) : launch_fwd_bf16<64, false>(p, grid_x, s);
@@ -164,6 +170,56 @@ extern "C" attn_status_t attn_fwd(const attn_fwd_args_t* a, void* stream) {
       case 64: return c ? launch_fwd_f32<64, true>(p, grid_x, s) : launch_fwd_f32<64, false>(p, grid_x, s);
       case 80: return c ? launch_fwd_f32<80, true>(p, grid_x, s) : launch_fwd_f32<80, false>(p, grid_x, s);
       case 128: return c ? launch_fwd_f32<128, true>(p, grid_x, s) : launch_fwd_f32<128, false>(p, grid_x, s);
+    }
+  }
+  return ATTN_ERR_UNSUPPORTED;
+}
+
+// ------------------------------------------------------------------ masked
+constexpr int64_t kMaskMaxRowBytes = int64_t(1) << 27;  // 32-bit lane offsets span 16 mask rows
+
+extern "C" attn_status_t attn_validate_fwd_masked(const attn_fwd_args_t* a, const attn_mask_t* m) {
+  const attn_status_t st = attn_validate_fwd(a);
+  if (st != ATTN_OK) return st;
+  if (!m) return ATTN_ERR_NULL;
+  if (m->kind != ATTN_MASK_BOOL && m->kind != ATTN_MASK_ADD_BF16) return ATTN_ERR_DTYPE;
+  if (a->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  const bool work = a->B > 0 && a->Hq > 0 && a->Lq > 0;
+  if (!work || a->Lk == 0) return ATTN_OK;
+  if (!m->data) return ATTN_ERR_NULL;
+  const int64_t es = m->kind == ATTN_MASK_BOOL ? 1 : 2;
+  if (!aligned16(m->data)) return ATTN_ERR_LAYOUT;
+  if (m->strides[0] < 0 || m->strides[1] < 0 || m->strides[2] < 0 || (m->strides[2] * es) % 16 != 0)
+    return ATTN_ERR_LAYOUT;
+  if (a->Lk % (16 / es) != 0) return ATTN_ERR_UNSUPPORTED;  // whole 16-byte chunks per mask row
+  if (m->strides[2] * es >= kMaskMaxRowBytes) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+extern "C" attn_status_t attn_fwd_masked(const attn_fwd_args_t* a, const attn_mask_t* m, void* stream) {
+  const attn_status_t st = attn_validate_fwd_masked(a, m);
+  if (st != ATTN_OK) return st;
+  if (a->B == 0 || a->Hq == 0 || a->Lq == 0) return ATTN_OK;
+  if (a->Lk == 0) return attn_fwd(a, stream);  // no keys: the mask has nothing to remove
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  FwdParams p = dense_fwd_params(a);
+  p.mask = m->data;
+  p.m_sb = m->strides[0];
+  p.m_sh = m->strides[1];
+  p.m_sq = m->strides[2];
+  const int grid_x = (int)(a->B * a->Hq);
+  const bool c = a->causal != 0;
+  if (m->kind == ATTN_MASK_BOOL) {
+    switch (a->d) {
+      case 64: return c ? launch_fwd_bf16<64, true, 1>(p, grid_x, s) : launch_fwd_bf16<64, false, 1>(p, grid_x, s);
+      case 80: return c ? launch_fwd_bf16<80, true, 1>(p, grid_x, s) : launch_fwd_bf16<80, false, 1>(p, grid_x, s);
+      case 128: return c ? launch_fwd_bf16<128, true, 1>(p, grid_x, s) : launch_fwd_bf16<128, false, 1>(p, grid_x, s);
+    }
+  } else {
+    switch (a->d) {
+      case 64: return c ? launch_fwd_bf16<64, true, 2>(p, grid_x, s) : launch_fwd_bf16<64, false, 2>(p, grid_x, s);
+      case 80: return c ? launch_fwd_bf16<80, true, 2>(p, grid_x, s) : launch_fwd_bf16<80, false, 2>(p, grid_x, s);
+      case 128: return c ? launch_fwd_bf16<128, true, 2>(p, grid_x, s) : launch_fwd_bf16<128, false, 2>(p, grid_x, s);
     }
   }
   return ATTN_ERR_UNSUPPORTED;
@@ -224,6 +280,9 @@ extern "C" attn_status_t attn_fwd_varlen(const attn_fwd_varlen_args_t* a, void* 
   p.cu_k = a->cu_seqlens_k;
   p.total_q = (int)a->total_q;
   p.total_k = (int)a->total_k;
+  p.mask = nullptr;
+  p.m_sb = p.m_sh = p.m_sq = 0;
+  p.inv_abs_scale = 0.f;
   p.scale_log2 = effective_scale(a->scale, a->d) * kLog2e;
   p.scale_log2_abs = std::fabs(p.scale_log2);
   p.neg_q = p.scale_log2 < 0.f ? 1 : 0;

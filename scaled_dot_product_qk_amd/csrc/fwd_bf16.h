@@ -60,6 +60,12 @@ struct FwdParams {
   const int* cu_q;
   const int* cu_k;
   int total_q, total_k;
+  // Attention mask [B, Hq, Lq, Lk] (NULL if none): element strides of
+  // (batch, head, query), key stride 1; uint8 (nonzero: the pair takes part)
+  // or bf16 (added to the scaled score).
+  const void* mask;
+  int64_t m_sb, m_sh, m_sq;
+  float inv_abs_scale;   // 1 / |scale|: an additive mask enters the raw score as mask / |scale|
   float scale_log2;      // scale * log2(e)
   float scale_log2_abs;  // |scale * log2(e)|
   int neg_q;             // scale < 0: Q's sign bits are flipped on load (exact)
@@ -148,6 +154,26 @@ struct Bf16FwdShape {
   static_assert(kBufBytes < 65536, "in-buffer LDS offsets must fit the instruction offset field");
 };
 
+// Attention-mask tiles (MK: 1 uint8 boolean, 2 bf16 additive): the
+// workgroup's query rows x the 64 keys of a tile, row-major, double buffered
+// after the key/value buffers, copied with the key/value tiles.
+template <int D, int MK>
+struct FwdMaskShape {
+  using S = Bf16FwdShape<D>;
+  static_assert(S::kCopiesPerWave + (MK == 0 ? 0 : S::kBR / (1024 / (S::kBC * (MK == 1 ? 1 : 2))) / S::kWaves) < 16,
+                "copies in flight per wave fit the simple vmcnt encoding");
+  static constexpr int kEs = MK == 1 ? 1 : 2;             // bytes per element
+  static constexpr int kRowBytes = S::kBC * kEs;           // 64 or 128
+  static constexpr int kChunkKeys = 16 / kEs;              // keys per 16-byte chunk
+  static constexpr int kChunksPerRow = kRowBytes / 16;
+  static constexpr int kTileBytes = S::kBR * kRowBytes;
+  static constexpr int kRowsPerCopy = 1024 / kRowBytes;
+  static constexpr int kCopies = MK == 0 ? 0 : S::kBR / kRowsPerCopy;
+  static constexpr int kCopiesPerWave = kCopies / S::kWaves;
+  static constexpr int kLdsBytes = MK == 0 ? 0 : 2 * kTileBytes;
+  static_assert(MK == 0 || kCopies % S::kWaves == 0, "mask copies split evenly over the waves");
+};
+
 // LDS layout of a key row: its 16-byte chunks are XOR-swizzled by the row
 // index so that the operand reads spread over all banks.
 //   K (A operand of S^T = K Q^T, 16 bytes of 32 consecutive rows per read):
@@ -192,10 +218,11 @@ constexpr float kRescaleLog2 = 8.0f;
 constexpr float kSumGuard = 256.f;
 static_assert(kSumGuard == float(1 << int(kRescaleLog2)), "guard is 2^kRescaleLog2");
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int MK = 0>
 __global__ __launch_bounds__(64 * Bf16FwdShape<D>::kWaves, Bf16FwdShape<D>::kGroupsPerCU) void
 attn_fwd_bf16_kernel(FwdParams p_in) {
   using S = Bf16FwdShape<D>;
+  using MS = FwdMaskShape<D, MK>;
   constexpr int NB = S::kNB;
   typedef __attribute__((address_space(3))) char lds_char;
   typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
@@ -288,6 +315,21 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
     cp_off[v] = (uint32_t)cp_row * cp_row_bytes + 16 * lc;
     cp_on[v] = lc < S::kChunks;
   }
+  // Mask copy plan: wave w fills mask-tile rows m_row0 .. m_row0 +
+  // MS::kCopiesPerWave * MS::kRowsPerCopy - 1; lane l -> row l / chunks-per-row,
+  // 16-byte chunk l % chunks-per-row.
+  const char* m_base = nullptr;
+  int64_t m_row_bytes = 0;
+  int m_lrow = 0, m_chunk = 0, m_row0 = 0;
+  uint32_t m_lds0 = 0;
+  if constexpr (MK != 0) {
+    m_base = reinterpret_cast<const char*>(p.mask) + (b * p.m_sb + h * p.m_sh) * MS::kEs;
+    m_row_bytes = p.m_sq * MS::kEs;
+    m_lrow = lane / MS::kChunksPerRow;
+    m_chunk = lane % MS::kChunksPerRow;
+    m_row0 = wave * MS::kCopiesPerWave * MS::kRowsPerCopy;
+    m_lds0 = (uint32_t)(uintptr_t)lds_b + S::kLdsBytes;
+  }
   // Full tiles copy without checks; the tile holding key Lk - 1 reads rows
   // beyond it from row Lk - 1 instead (in bounds and finite), and those keys
   // are masked to -inf, so they carry weight 0.
@@ -310,6 +352,21 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
         if (S::kChunks == S::kPitch || cp_on[j % S::kKVar])
           fwd_copy16(cp_src + (int64_t)row0 * cp_st, (uint32_t)(row - row0) * cp_row_bytes + cp_chunk16[j % S::kKVar],
                      dst + j * S::kRowsPerCopy * S::kRowBytes);
+      }
+    }
+    if constexpr (MK != 0) {
+      // Mask rows q0 + m_row0 + ... of this tile's 64 keys.  Every lane
+      // copies (rows past Lq repeat row Lq - 1, chunks past Lk repeat the
+      // last chunk; both are masked anyway), so each wave issues exactly
+      // MS::kCopiesPerWave copies per tile.
+      const uint32_t mdst = m_lds0 + (t & 1) * MS::kTileBytes;
+      const int kc0 = min(kv0 + m_chunk * MS::kChunkKeys, p.Lk - MS::kChunkKeys);
+#pragma unroll
+      for (int j = 0; j < MS::kCopiesPerWave; ++j) {
+        const int r = q0 + m_row0 + MS::kRowsPerCopy * j;
+        const int ra = min(r, p.Lq - 1), rl = min(r + m_lrow, p.Lq - 1);
+        fwd_copy16(m_base + (int64_t)ra * m_row_bytes, (uint32_t)(rl - ra) * (uint32_t)m_row_bytes + kc0 * MS::kEs,
+                   mdst + (m_row0 + MS::kRowsPerCopy * j) * MS::kRowBytes);
       }
     }
   };
@@ -417,7 +474,9 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
     // P = exp2(c s - m) for half sb of row block nb, packed as two P^T B
     // operands; returns this lane's share of the half's row sum.
     auto exp_half = [&](int sb, int nb) {
-      const float neg_m = -m_run[nb];
+      // (with an attention mask a row may still have no visible key: its
+      // reference stays -inf and every probability is exp2(-inf) = 0)
+      const float neg_m = (MK != 0 && m_run[nb] == kNegInf) ? 0.f : -m_run[nb];
       float rs[4] = {0.f, 0.f, 0.f, 0.f};  // short dependency chains
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -450,12 +509,39 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
             s[nb][sb][r] = vis ? s[nb][sb][r] : kNegInf;
           }
       }
+      if constexpr (MK != 0) {
+        // Keys 32 sb + 8 j + 4 g + 0..3 of this lane's query row in the mask
+        // tile: a boolean removes pairs, an additive mask enters the raw score
+        // as mask / |scale| (so the exponent gets scale s + mask, in log2 units).
+        const lds_char* mt = lds_b + S::kLdsBytes + buf * MS::kTileBytes;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const lds_char* mrow = mt + (wave * S::kRowsPerWave + 32 * nb + lq) * MS::kRowBytes;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int off = (32 * sb + 8 * j + 4 * g) * MS::kEs;
+            if constexpr (MK == 1) {
+              const uint32_t w = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(mrow + off);
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                s[nb][sb][4 * j + e] = ((w >> (8 * e)) & 0xffu) ? s[nb][sb][4 * j + e] : kNegInf;
+            } else {
+              const u32x2 w = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(mrow + off);
+              s[nb][sb][4 * j + 0] = __builtin_fmaf(bf16_lo(w[0]), p.inv_abs_scale, s[nb][sb][4 * j + 0]);
+              s[nb][sb][4 * j + 1] = __builtin_fmaf(bf16_hi(w[0]), p.inv_abs_scale, s[nb][sb][4 * j + 1]);
+              s[nb][sb][4 * j + 2] = __builtin_fmaf(bf16_lo(w[1]), p.inv_abs_scale, s[nb][sb][4 * j + 2]);
+              s[nb][sb][4 * j + 3] = __builtin_fmaf(bf16_hi(w[1]), p.inv_abs_scale, s[nb][sb][4 * j + 3]);
+            }
+          }
+        }
+      }
       float ls[NB];
       bool redo = false;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         ls[nb] = exp_half(sb, nb);
-        redo = redo || !(ls[nb] <= kSumGuard);
+        // a row still without a visible key always takes the exact path
+        redo = redo || !(ls[nb] <= kSumGuard) || (MK != 0 && m_run[nb] == kNegInf);
       }
       // about 60 vector instructions per row block: one product per share
 #pragma unroll
@@ -504,7 +590,7 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
   if (n_tiles > 0) issue_tile(0);
   if (n_tiles > 1) {
     issue_tile(1);
-    __builtin_amdgcn_s_waitcnt(0x0f70 | S::kCopiesPerWave);  // vmcnt: tile 0's copies done
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (S::kCopiesPerWave + MS::kCopiesPerWave));  // vmcnt: tile 0's copies done
   } else {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   }

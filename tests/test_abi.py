@@ -305,3 +305,42 @@ def test_bwd_workspace_rules():
     assert L.attn_bwd(ctypes.byref(bwd_args(B=0)), None, 0, None) == OK
     assert L.attn_bwd(ctypes.byref(bwd_args(Lq=0, Lk=0)), None, 0, None) == OK
     assert L.attn_validate_bwd(None) == NULL
+
+
+def mask_args(**kw):
+    m = sdpa.MaskArgs()
+    m.data = kw.get("data", P + 0x70000000)
+    m.kind = kw.get("kind", sdpa.ATTN_MASK_BOOL)
+    m.strides = sdpa._i64x3(*kw.get("ms", (0, 0, 320)))
+    return m
+
+
+def vmask(fkw=None, **kw):
+    return sdpa.lib().attn_validate_fwd_masked(ctypes.byref(fwd_args(**(fkw or {}))), ctypes.byref(mask_args(**kw)))
+
+
+@pytest.mark.parametrize("kind", [1, 2])
+@pytest.mark.parametrize("d", [64, 80, 128])
+def test_masked_valid(kind, d):
+    assert vmask(dict(d=d, Lk=320, Lq=300, ks=(2 * 320 * d, 320 * d, d), vs=(2 * 320 * d, 320 * d, d)),
+                 kind=kind) == OK
+
+
+@pytest.mark.parametrize("fkw,kw,status", [
+    (None, dict(kind=0), DTYPE), (None, dict(kind=3), DTYPE), (None, dict(data=0), NULL),
+    (dict(dtype=1), dict(), UNSUP), (None, dict(data=P + 8), LAYOUT), (None, dict(ms=(0, 0, 303)), LAYOUT),
+    (None, dict(ms=(-1, 0, 320)), LAYOUT),
+    (None, dict(), UNSUP),                                   # Lk = 300 is not a multiple of 16
+    (dict(Lk=320, Lq=320, ks=(2 * 320 * 64, 320 * 64, 64), vs=(2 * 320 * 64, 320 * 64, 64)),
+     dict(ms=(0, 0, 2 ** 27)), UNSUP),                       # mask rows too far apart
+    (dict(Lk=320, Lq=320, ks=(2 * 320 * 64, 320 * 64, 64), vs=(2 * 320 * 64, 320 * 64, 64)),
+     dict(kind=2, ms=(0, 0, 324)), LAYOUT),                  # bf16 rows must start on 16 bytes
+])
+def test_masked_rejections(fkw, kw, status):
+    assert vmask(fkw, **kw) == status
+    assert sdpa.lib().attn_fwd_masked(ctypes.byref(fwd_args(**(fkw or {}))), ctypes.byref(mask_args(**kw)),
+                                      None) == status
+
+
+def test_masked_null_mask_struct():
+    assert sdpa.lib().attn_validate_fwd_masked(ctypes.byref(fwd_args()), None) == NULL

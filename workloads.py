@@ -161,6 +161,17 @@ def make_varlen_inputs(w: VarlenWorkload, lens_q=None, lens_k=None):
     return q.to(dt), k.to(dt), v.to(dt), cu_q, cu_k
 
 
+def make_mask(shape, kind: str, seed: int, keep: float = 0.7):
+    """A seeded attention mask of the given [B|1, H|1, Lq, Lk] shape: "bool"
+    keeps each pair with probability `keep`; "add" draws N(0, 1) * 2 values
+    rounded to bf16."""
+    g = torch.Generator().manual_seed(seed)
+    u = torch.rand(shape, generator=g, dtype=torch.float32)
+    if kind == "bool":
+        return u < keep
+    return (torch.randn(shape, generator=g, dtype=torch.float32) * 2.0).to(torch.bfloat16)
+
+
 def shrink(w, **kw):
     """A copy of a workload with some sizes replaced (name and seed kept unless given)."""
     return replace(w, **kw)
