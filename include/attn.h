@@ -110,7 +110,7 @@ typedef struct {
   int64_t strides[3];   /* element strides of (batch, head, query); 0 broadcasts */
 } attn_mask_t;
 
-/* Packed variable-length prefill ("Flash Attention原理：分块计算与重计算"/* Packed variable-length prefill ("Flash Attention原理：分块计算与重计算"
+/* Packed variable-length prefill ("Flash Attention原理：分块计算与重计算"
  * (cnblogs), FAQ Q10: several sequences of different lengths packed into one
  * batch through cumulative sequence offsets, no padding; FAQ Q15: queries and
  * keys/values of different lengths, as in cross-attention).  Sequence b owns
@@ -162,7 +162,7 @@ typedef struct {
   float scale;     /* as in the forward; 0 selects 1/sqrt(d) */
 } attn_bwd_args_t;
 
-/* Decode: one query token per sequence against a ragged KV cache. *//* Decode: one query token per sequence against a ragged KV cache. */
+/* Decode: one query token per sequence against a ragged KV cache. */
 typedef struct {
   const void *q;          /* [B, Hq, d] */
   const void *k_cache;    /* [B, Hkv, Lmax, d]; slots >= seqlens[b] are never read */
@@ -205,7 +205,6 @@ attn_status_t attn_fwd(const attn_fwd_args_t *args, void *stream);
 attn_status_t attn_fwd_masked(const attn_fwd_args_t *args, const attn_mask_t *mask, void *stream);
 
 /*
- * attn_fwd_varlen - packed variable-length prefill, one kernel launch: the/*
  * attn_fwd_varlen - packed variable-length prefill, one kernel launch: the
  * same computation as attn_fwd applied to each sequence separately.
  * Supported: dtype bf16; d in {64, 80, 128}; Hq % Hkv == 0;
@@ -266,7 +265,6 @@ attn_status_t attn_bwd(const attn_bwd_args_t *args, void *workspace, size_t work
                        void *stream);
 
 /* Argument checks only (no device work, no HIP call): the status attn_fwd /
- * attn_decode would return before launching.  Usable without a GPU. *//* Argument checks only (no device work, no HIP call): the status attn_fwd /
  * attn_decode would return before launching.  Usable without a GPU. */
 attn_status_t attn_validate_fwd(const attn_fwd_args_t *args);
 attn_status_t attn_validate_fwd_masked(const attn_fwd_args_t *args, const attn_mask_t *mask);

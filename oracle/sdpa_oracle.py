@@ -37,7 +37,13 @@ notes):
     the textbook chain rule through S, P and O, which the pages do not write
     out: dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(P * dP)),
     dQ = scale dS K, dK = scale dS^T Q; a grouped key/value head receives the
-    sum over its query heads.
+    sum over its query heads;
+  * FP8 inputs (cnblogs section 六 and FAQ Q8: the third version runs on
+    8-bit floating-point matrix units; the pages fix no format and no
+    scaling): every element is an e4m3 code and every tensor carries one
+    float multiplier, its descale, so an element stands for descale times the
+    code's value; the attention is the definition above applied to those
+    values.
 
 All functions take and return numpy float64 arrays.
 """
@@ -468,3 +474,55 @@ def brute_force_attention(q, k, v, causal: bool = False, scale: Optional[float] 
         O.append(Ob)
         LSE.append(Lb)
     return O, LSE
+
+
+# ---------------------------------------------------------------------------
+# FP8 inputs.  An e4m3 code is 1 sign bit, 4 exponent bits (bias 7) and 3
+# mantissa bits: exponent field e in 1..15 gives (1 + m/8) 2^(e-7), field 0
+# gives the subnormals (m/8) 2^-6, and the one pattern with every exponent and
+# mantissa bit set is not a number (there is no infinity).  The largest finite
+# value is 1.75 * 2^8 = 448.
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values of e4m3 codes (uint8, any shape) as float64."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c & 0x80) != 0, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    subnormal = (m / 8.0) * 2.0 ** -6
+    val = sign * np.where(e == 0, subnormal, normal)
+    return np.where((e == 15) & (c & 0x7 == 7), np.nan, val)
+
+
+def dequantize_e4m3(codes, descale: float) -> np.ndarray:
+    """The values a tensor of e4m3 codes stands for: descale * value(code)."""
+    if hasattr(codes, "numpy"):
+        codes = codes.numpy()
+    return e4m3_decode(codes) * float(descale)
+
+
+def attention_forward_fp8(q8, k8, v8, q_descale: float, k_descale: float, v_descale: float,
+                          causal: bool = False, scale: Optional[float] = None,
+                          threads: Optional[int] = None):
+    """Prefill attention of FP8 inputs: q8 [B,Hq,Lq,d], k8 and v8 [B,Hkv,Lk,d]
+    e4m3 codes with one descale each.  Exactly attention_forward applied to
+    the dequantised values; returns O [B,Hq,Lq,d] and LSE [B,Hq,Lq]."""
+    return attention_forward(dequantize_e4m3(q8, q_descale), dequantize_e4m3(k8, k_descale),
+                             dequantize_e4m3(v8, v_descale), causal=causal, scale=scale,
+                             threads=threads)
+
+
+def attention_forward_fp8_rows(q8, k8, v8, q_descale: float, k_descale: float, v_descale: float,
+                               b: int, h: int, rows: Iterable[int], causal: bool = False,
+                               scale: Optional[float] = None):
+    """attention_forward_fp8 for a few query rows of one (batch, query head);
+    only that head's codes are dequantised.  Returns O [len(rows), d], LSE."""
+    Hq, Hkv = q8.shape[1], k8.shape[1]
+    hk = h // (Hq // Hkv)
+    rows = np.asarray(list(rows), dtype=np.int64)
+    if scale is None:
+        scale = default_scale(q8.shape[-1])
+    q = dequantize_e4m3(q8[b, h], q_descale)[rows]
+    return _head_attention(q, dequantize_e4m3(k8[b, hk], k_descale), dequantize_e4m3(v8[b, hk], v_descale),
+                           scale, causal, row_ids=rows)

@@ -579,3 +579,117 @@ def test_planted_backward_mistakes(monkeypatch, kind):
         except AssertionError:
             failures += 1
     assert failures >= 1, f"planted backward mistake {kind} not caught"
+
+
+# ---------------------------------------------------------- P-18 FP8 inputs
+def test_e4m3_decode_matches_torch_and_the_format():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = orc.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(ours, ref, equal_nan=True)
+    # closed forms of the format: unit, largest, smallest subnormal, smallest normal, NaN, -0
+    assert ours[0x38] == 1.0 and ours[0xb8] == -1.0 and ours[0x7e] == 448.0 and ours[0xfe] == -448.0
+    assert ours[0x01] == 2.0 ** -9 and ours[0x07] == 7 * 2.0 ** -9 and ours[0x08] == 2.0 ** -6
+    assert np.isnan(ours[0x7f]) and np.isnan(ours[0xff]) and ours[0x80] == 0 and np.signbit(ours[0x80])
+    # the 127 non-negative finite codes are strictly increasing; the sign bit mirrors them
+    pos = ours[:0x7f]
+    assert np.all(np.diff(pos) > 0) and np.array_equal(ours[0x80:0xff], -pos)
+    # 8 codes per binade, evenly spaced: binade e (codes 8e .. 8e+7) steps by 2^(e-10), the
+    # subnormals by 2^-9 like binade 1
+    step = np.diff(pos)
+    assert (step[:8] == 2.0 ** -9).all()
+    for e in range(1, 16):
+        assert (step[8 * e: min(8 * e + 7, 126)] == 2.0 ** (e - 10)).all()
+
+
+# values of a few codes, from the format's definition worked by hand
+E4M3_BY_HAND = {0x00: 0.0, 0x38: 1.0, 0xb8: -1.0, 0x40: 2.0, 0xc0: -2.0, 0x30: 0.5, 0xb0: -0.5,
+                0x3c: 1.5, 0x44: 3.0, 0xc4: -3.0, 0x04: 2.0 ** -7, 0x2e: 0.4375}
+
+
+def _hand_codes(shape, seed):
+    keys = np.array(sorted(E4M3_BY_HAND), dtype=np.uint8)
+    return np.random.default_rng(seed).choice(keys, size=shape).astype(np.uint8)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_attention_matches_brute_force_on_hand_decoded_values(causal):
+    q8, k8, v8 = _hand_codes((1, 4, 6, 8), 160), _hand_codes((1, 2, 7, 8), 161), _hand_codes((1, 2, 7, 8), 162)
+    dq, dk, dv = 0.75, 1.25, -0.5
+    o, lse = orc.attention_forward_fp8(q8, k8, v8, dq, dk, dv, causal=causal)
+    val = np.vectorize(lambda c: E4M3_BY_HAND[int(c)])
+    ob, lb = orc.brute_force_attention((val(q8) * dq).tolist(), (val(k8) * dk).tolist(), (val(v8) * dv).tolist(),
+                                       causal=causal)
+    assert np.abs(o - np.array(ob)).max() <= 1e-12 and np.abs(lse - np.array(lb)).max() <= 1e-12
+
+
+def test_fp8_descale_invariants():
+    r = np.random.default_rng(163)
+    q8, k8, v8 = (r.integers(0, 256, (1, 2, 9, 16)) for _ in range(3))
+    q8, k8, v8 = (np.where((c & 0x7f) == 0x7f, 0, c).astype(np.uint8) for c in (q8, k8, v8))  # no NaN codes
+    o, lse = orc.attention_forward_fp8(q8, k8, v8, 0.01, 0.02, 0.03, causal=True)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    # the scores see only the product q_descale * k_descale * scale
+    o1, l1 = orc.attention_forward_fp8(q8, k8, v8, 0.02, 0.01, 0.03, causal=True)
+    o2, l2 = orc.attention_forward_fp8(q8, k8, v8, 0.0002, 1.0, 0.03, causal=True, scale=0.25)
+    for a, b in ((o1, o), (o2, o)):
+        assert np.abs(a - b).max() <= 1e-12 * max(1.0, np.abs(o).max())
+    assert np.abs(l1 - lse).max() <= 1e-12 and np.abs(l2 - lse).max() <= 1e-12
+    # O is linear in the value descale, LSE does not see it
+    o3, l3 = orc.attention_forward_fp8(q8, k8, v8, 0.01, 0.02, 0.06, causal=True)
+    assert np.array_equal(o3, 2 * o) and np.array_equal(l3, lse)
+    # the rows helper is the same definition
+    orow, lrow = orc.attention_forward_fp8_rows(q8, k8, v8, 0.01, 0.02, 0.03, 0, 1, [0, 4, 8], causal=True)
+    assert np.abs(orow - o[0, 1, [0, 4, 8]]).max() <= 1e-13 and np.abs(lrow - lse[0, 1, [0, 4, 8]]).max() <= 1e-13
+
+
+def test_fp8_recipe_codes_stand_for_the_drawn_values():
+    w = wl.shrink(wl.C8, Lq=40, Lk=40)
+    q8, k8, v8, ds = wl.make_fp8_inputs(w)
+    g = torch.Generator().manual_seed(w.seed)
+    x = torch.randn((w.B, w.Hq, w.Lq, w.d), generator=g, dtype=torch.float32).double().numpy()
+    deq = orc.dequantize_e4m3(q8, ds[0])
+    # every code is the nearest e4m3 value: within half a step (2^-4 relative, 2^-10 absolute at the bottom)
+    err = np.abs(deq - x) / ds[0]
+    assert (err <= np.maximum(np.abs(x / ds[0]) * 2.0 ** -4, 2.0 ** -10) * (1 + 1e-6)).all()
+    assert np.abs(deq).max() == pytest.approx(np.abs(x).max(), rel=1e-6)  # the largest maps to 448
+
+
+def _fp8_mutant(kind):
+    def f(codes):
+        c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+        sign = np.where((c & 0x80) != 0, -1.0, 1.0)
+        e, m = (c >> 3) & 0xF, (c & 7).astype(np.float64)
+        bias = 8.0 if kind == "bias_8" else 7.0
+        normal = (1.0 + m / 8.0) * np.exp2(e - bias)
+        sub = (m / 8.0) * 2.0 ** (-6 if kind != "subnormal_exponent" else -7)
+        if kind == "no_subnormals":
+            sub = np.zeros_like(sub)
+        val = sign * np.where(e == 0, sub, normal)
+        if kind == "sign_ignored":
+            val = np.abs(val)
+        return np.where((e == 15) & ((c & 7) == 7), np.nan, val)
+    return f
+
+
+@pytest.mark.parametrize("kind", ["bias_8", "subnormal_exponent", "no_subnormals", "sign_ignored", "v_descale_dropped"])
+def test_planted_fp8_mistakes(monkeypatch, kind):
+    if kind == "v_descale_dropped":
+        real = orc.dequantize_e4m3
+        calls = []
+
+        def deq(codes, descale):
+            calls.append(descale)
+            return real(codes, 1.0 if len(calls) % 3 == 0 else descale)
+        monkeypatch.setattr(orc, "dequantize_e4m3", deq)
+    else:
+        monkeypatch.setattr(orc, "e4m3_decode", _fp8_mutant(kind))
+    failures = 0
+    for fn in (test_e4m3_decode_matches_torch_and_the_format,
+               lambda: test_fp8_attention_matches_brute_force_on_hand_decoded_values(True),
+               test_fp8_descale_invariants):
+        try:
+            fn()
+        except AssertionError:
+            failures += 1
+    assert failures >= 1, f"planted FP8 mistake {kind} not caught"

@@ -11,6 +11,10 @@ Recipe (one per workload):
                   torch's own conversion); the oracle receives exactly those
                   values widened to float64
   decode workloads, after V: lengths = randint(lo, hi + 1, (B,), generator=g)
+  FP8 workloads: Q, K, V drawn as above, each then stored as e4m3 codes of
+                  x / descale with descale = max|x| / 448 (torch's
+                  float8_e4m3fn rounding); the oracle receives the codes and
+                  the descales
   packed variable-length workloads: lengths = randint(lo, hi + 1, (B,),
                   generator=g) first (query and key lengths equal unless
                   given), then Q [total_q, Hq, d], K, V [total_k, Hkv, d]
@@ -96,7 +100,12 @@ class VarlenWorkload:
 C6 = VarlenWorkload("varlen_bf16_causal_gqa_b16_hq32_hkv8_len256_4096_d128", 16, 32, 8, 256, 4096, 128,
                     "bf16", True, 1006)
 
+# FP8 (e4m3) inputs at the shapes of the n=4096 and the n=8192 workloads.
+C7 = FwdWorkload("fwd_fp8_b1_h96_n4096_d64", 1, 96, 96, 4096, 4096, 64, "fp8", False, 1011)
+C8 = FwdWorkload("fwd_fp8_causal_gqa_b1_hq32_hkv8_n8192_d128", 1, 32, 8, 8192, 8192, 128, "fp8", True, 1012)
+
 FWD_WORKLOADS = {w.name: w for w in (C1, C2, C3, C4)}
+FP8_WORKLOADS = {w.name: w for w in (C7, C8)}
 DECODE_WORKLOADS = {C5.name: C5}
 
 
@@ -118,6 +127,33 @@ def make_fwd_inputs(w: FwdWorkload, q_mul: float = 1.0):
         q = q * q_mul
     dt = torch_dtype(w.dtype)
     return q.to(dt), k.to(dt), v.to(dt)
+
+
+E4M3_MAX = 448.0  # largest finite e4m3 value
+
+
+def make_fp8_inputs(w: FwdWorkload, q_mul: float = 1.0):
+    """e4m3 codes (uint8) q8 [B,Hq,Lq,d], k8 and v8 [B,Hkv,Lk,d] on the CPU and
+    their descales (q_descale, k_descale, v_descale).
+
+    Q, K and V are drawn as make_fwd_inputs draws them (float32, same order,
+    Q times q_mul); each tensor gets descale = max|x| / 448 and codes =
+    torch's float8_e4m3fn rounding of x / descale, so the codes span the
+    format's range and a code stands for descale times its value.
+    """
+    g = torch.Generator().manual_seed(w.seed)
+    xs = [torch.randn((w.B, w.Hq, w.Lq, w.d), generator=g, dtype=torch.float32),
+          torch.randn((w.B, w.Hkv, w.Lk, w.d), generator=g, dtype=torch.float32),
+          torch.randn((w.B, w.Hkv, w.Lk, w.d), generator=g, dtype=torch.float32)]
+    if q_mul != 1.0:
+        xs[0] = xs[0] * q_mul
+    codes, descales = [], []
+    for x in xs:
+        amax = float(x.abs().max()) if x.numel() else 1.0
+        ds = amax / E4M3_MAX if amax > 0 else 1.0
+        codes.append((x / ds).to(torch.float8_e4m3fn).view(torch.uint8))
+        descales.append(ds)
+    return codes[0], codes[1], codes[2], tuple(descales)
 
 
 def make_decode_inputs(w: DecodeWorkload, poison_tail: bool = False,
