@@ -7,10 +7,11 @@ One step = one pass of the whole path over synthetic, HBM-resident inputs:
 Each call is timed with HIP events recorded on the stream the kernels run on;
 the step as a whole is timed with host clocks between device synchronisations.
 After the step loop, attn_fwd_varlen on 16 packed causal GQA sequences of
-256..4096 tokens (d=128), attn_bwd on the causal GQA n=8192 d=128 workload and
+256..4096 tokens (d=128), attn_bwd on the causal GQA n=8192 d=128 workload,
 attn_fwd_masked on the n=4096 d=64 workload with one boolean mask shared by
-all heads are timed the same way, each on its own, and reported in `extra`
-(they are not part of the step).
+all heads, and attn_fwd_fp8 on e4m3 versions of the two prefill workloads are
+timed the same way, each on its own, and reported in `extra` (they are not
+part of the step).
 
 Prints ONE JSON line.  `value` is the headline workload's attention-forward
 throughput in TFLOP/s (credited flops 4 n^2 d H B, halved when causal).
@@ -34,10 +35,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 matrix peak (twice the bf16 rate)
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E peak
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "scaled_dot_product_qk_amd", "csrc", f)
-                  for f in ("attn_api.hip", "device_common.h", "fwd_bf16.h", "fwd_f32.h", "decode.h", "bwd_bf16.h")]
+                  for f in ("attn_api.hip", "device_common.h", "fwd_bf16.h", "fwd_f32.h", "fwd_fp8.h", "decode.h",
+                            "bwd_bf16.h")]
 
 
 def kernel_source_hash() -> str:
@@ -74,7 +77,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["all", "fwd_n4096", "fwd_causal_n8192", "decode", "fwd_varlen", "bwd",
-                                       "fwd_masked"],
+                                       "fwd_masked", "fwd_fp8_n4096", "fwd_fp8_causal_n8192"],
                     default="all",
                     help="time one call of the step only (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -128,13 +131,11 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
 
+    SOLO = ("fwd_varlen", "bwd", "fwd_masked", "fwd_fp8_n4096", "fwd_fp8_causal_n8192")
     names = ["fwd_n4096", "fwd_causal_n8192", "decode"] if args.only == "all" else \
-        ([] if args.only in ("fwd_varlen", "bwd", "fwd_masked") else [args.only])
-    with_varlen = args.only in ("all", "fwd_varlen")
-    with_bwd = args.only in ("all", "bwd")
-    with_masked = args.only in ("all", "fwd_masked")
-    solo = (["fwd_varlen"] if with_varlen else []) + (["bwd"] if with_bwd else []) + \
-        (["fwd_masked"] if with_masked else [])
+        ([] if args.only in SOLO else [args.only])
+    solo = [n for n in SOLO if args.only in ("all", n)]
+    with_varlen, with_bwd, with_masked = ("fwd_varlen" in solo), ("bwd" in solo), ("fwd_masked" in solo)
 
     # ---- inputs, generated on the host and copied once to HBM ----
     calls = {}
@@ -187,6 +188,16 @@ def main():
         om = torch.empty_like(GM[0])
         lm = torch.empty(GM[0].shape[:3], dtype=torch.float32, device=dev)
         calls["fwd_masked"] = lambda: sdpa.attn_fwd_masked(*GM, mm, out=om, lse=lm, stream=stream)
+    fp8_in = {}
+    for n, w in (("fwd_fp8_n4096", wl.C7), ("fwd_fp8_causal_n8192", wl.C8)):
+        if n in solo:
+            q8, k8, v8, ds8 = wl.make_fp8_inputs(w)
+            G8 = [t.to(dev) for t in (q8, k8, v8)]
+            o8 = torch.empty(G8[0].shape, dtype=torch.bfloat16, device=dev)
+            l8 = torch.empty(G8[0].shape[:3], dtype=torch.float32, device=dev)
+            fp8_in[n] = (w, G8)
+            calls[n] = (lambda G8=G8, ds8=ds8, o8=o8, l8=l8, c=w.causal:
+                        sdpa.attn_fwd_fp8(*G8, ds8, causal=c, out=o8, lse=l8, stream=stream))
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -263,10 +274,20 @@ def main():
                              "algorithmic_bytes": wl.algorithmic_bytes_fwd(C2.B, C2.Hq, C2.Hkv, C2.Lq, C2.Lk, C2.d, 2)
                              + C2.Lq * C2.Lk}
 
-    def roof_fwd(r, tag):
+    for n, (w, _) in fp8_in.items():
+        if n in ms:
+            t = ms[n] / 1e3
+            ff = wl.algorithmic_flops_fwd(w.B, w.Hq, w.Lq, w.Lk, w.d, w.causal)
+            res[n] = {"kernel": f"attn_fwd_fp8_kernel<{w.d}, {'true' if w.causal else 'false'}>", "ms": ms[n],
+                      "tflops": ff / t / 1e12, "algorithmic_flops": ff,
+                      "algorithmic_bytes": wl.algorithmic_bytes_fwd(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.d, 1)
+                      + w.B * w.Hq * w.Lq * w.d,  # O is bf16: one more byte per element
+                      "workload": w.name}
+
+    def roof_fwd(r, tag, peak=PEAK_BF16_TFLOPS):
         tr = counted_traffic(tag)
-        return {"bound": "mfma", "achieved": r["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": r["tflops"] / PEAK_BF16_TFLOPS, "traffic": tr}
+        return {"bound": "mfma", "achieved": r["tflops"], "peak": peak, "unit": "TFLOP/s",
+                "frac": r["tflops"] / peak, "traffic": tr}
 
     headline = res.get("fwd_n4096")
     out = {
@@ -304,6 +325,13 @@ def main():
     if "bwd" in res:
         r = res["bwd"]
         out["extra"]["bwd_causal_gqa_n8192_d128"] = dict(r, roofline=roof_fwd(r, "attn_bwd_d128_causal_n8192"))
+    if "fwd_fp8_n4096" in res:
+        r = res["fwd_fp8_n4096"]
+        out["extra"]["fwd_fp8_n4096_d64"] = dict(r, roofline=roof_fwd(r, "attn_fwd_fp8_d64_n4096", PEAK_FP8_TFLOPS))
+    if "fwd_fp8_causal_n8192" in res:
+        r = res["fwd_fp8_causal_n8192"]
+        out["extra"]["fwd_fp8_causal_gqa_n8192_d128"] = dict(
+            r, roofline=roof_fwd(r, "attn_fwd_fp8_d128_causal_n8192", PEAK_FP8_TFLOPS))
     if headline:
         out["extra"]["fwd_n4096_d64"] = headline
     if not args.no_cpu_baseline and args.only in ("all", "fwd_n4096"):

@@ -162,6 +162,29 @@ typedef struct {
   float scale;     /* as in the forward; 0 selects 1/sqrt(d) */
 } attn_bwd_args_t;
 
+/* FP8 prefill ("Flash Attention原理：分块计算与重计算" (cnblogs), section 六
+ * and FAQ Q8: the products run on 8-bit floating-point matrix units).  Q, K
+ * and V are e4m3 codes (1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+ * bits, subnormals, largest value 448, no infinity; S.1111.111 is NaN), one
+ * byte each; every tensor carries one fp32 descale and an element stands for
+ * descale * value(code).  Scores are scale * q_descale * k_descale * (codes
+ * product); O is written in bf16. */
+typedef struct {
+  const void *q;   /* [B, Hq,  Lq, d] e4m3 codes */
+  const void *k;   /* [B, Hkv, Lk, d] e4m3 codes */
+  const void *v;   /* [B, Hkv, Lk, d] e4m3 codes */
+  void *o;         /* [B, Hq,  Lq, d] bf16 */
+  float *lse;      /* [B, Hq, Lq] fp32, contiguous */
+  int64_t B, Hq, Hkv, Lq, Lk, d;
+  int64_t q_strides[3];  /* element (= byte) strides of (batch, head, token), multiples of 16 */
+  int64_t k_strides[3];
+  int64_t v_strides[3];
+  int64_t o_strides[3];  /* bf16 element strides, multiples of 8 */
+  float q_descale, k_descale, v_descale;  /* finite */
+  int32_t causal;  /* nonzero: query i sees keys j <= i (top-left, any Lq and Lk) */
+  float scale;     /* multiplier of Q K^T; 0 selects 1/sqrt(d) */
+} attn_fwd_fp8_args_t;
+
 /* Decode: one query token per sequence against a ragged KV cache. */
 typedef struct {
   const void *q;          /* [B, Hq, d] */
@@ -203,6 +226,20 @@ attn_status_t attn_fwd(const attn_fwd_args_t *args, void *stream);
  * to the traffic (strides 0 share one mask between heads or batches).
  */
 attn_status_t attn_fwd_masked(const attn_fwd_args_t *args, const attn_mask_t *mask, void *stream);
+
+/*
+ * attn_fwd_fp8 - prefill attention forward on FP8 inputs, one kernel launch.
+ * Both products run on the e4m3 matrix cores with fp32 accumulation; the
+ * softmax runs in fp32; each probability is rounded to e4m3 (nearest even)
+ * before the P V product and the row normaliser sums the rounded values, so
+ * O = v_descale * sum_j P~_j V_j / sum_j P~_j exactly up to accumulation,
+ * rounded to bf16, and LSE = m + ln(sum_j P~_j).  Supported: d in {64, 128};
+ * Hq % Hkv == 0; Lq and Lk independent, causal or not.  Limits as attn_fwd
+ * (K and V token strides below 2^28 bytes).  B, Hq or Lq of 0 launches
+ * nothing; Lk == 0 gives O = 0 and LSE = -inf.  A non-finite descale or scale, or a
+ * score multiplier past the float range, is ATTN_ERR_SHAPE.
+ */
+attn_status_t attn_fwd_fp8(const attn_fwd_fp8_args_t *args, void *stream);
 
 /*
  * attn_fwd_varlen - packed variable-length prefill, one kernel launch: the
@@ -269,6 +306,7 @@ attn_status_t attn_bwd(const attn_bwd_args_t *args, void *workspace, size_t work
 attn_status_t attn_validate_fwd(const attn_fwd_args_t *args);
 attn_status_t attn_validate_fwd_masked(const attn_fwd_args_t *args, const attn_mask_t *mask);
 attn_status_t attn_validate_fwd_varlen(const attn_fwd_varlen_args_t *args);
+attn_status_t attn_validate_fwd_fp8(const attn_fwd_fp8_args_t *args);
 attn_status_t attn_validate_bwd(const attn_bwd_args_t *args);
 attn_status_t attn_validate_decode(const attn_decode_args_t *args);
 

@@ -504,20 +504,22 @@ def dequantize_e4m3(codes, descale: float) -> np.ndarray:
 
 def attention_forward_fp8(q8, k8, v8, q_descale: float, k_descale: float, v_descale: float,
                           causal: bool = False, scale: Optional[float] = None,
-                          threads: Optional[int] = None):
+                          threads: Optional[int] = None, return_sp: bool = False):
     """Prefill attention of FP8 inputs: q8 [B,Hq,Lq,d], k8 and v8 [B,Hkv,Lk,d]
     e4m3 codes with one descale each.  Exactly attention_forward applied to
-    the dequantised values; returns O [B,Hq,Lq,d] and LSE [B,Hq,Lq]."""
+    the dequantised values; returns O [B,Hq,Lq,d] and LSE [B,Hq,Lq] (and S, P
+    with return_sp)."""
     return attention_forward(dequantize_e4m3(q8, q_descale), dequantize_e4m3(k8, k_descale),
                              dequantize_e4m3(v8, v_descale), causal=causal, scale=scale,
-                             threads=threads)
+                             threads=threads, return_sp=return_sp)
 
 
 def attention_forward_fp8_rows(q8, k8, v8, q_descale: float, k_descale: float, v_descale: float,
                                b: int, h: int, rows: Iterable[int], causal: bool = False,
-                               scale: Optional[float] = None):
+                               scale: Optional[float] = None, return_sp: bool = False):
     """attention_forward_fp8 for a few query rows of one (batch, query head);
-    only that head's codes are dequantised.  Returns O [len(rows), d], LSE."""
+    only that head's codes are dequantised.  Returns O [len(rows), d], LSE
+    (and the rows of S and P with return_sp)."""
     Hq, Hkv = q8.shape[1], k8.shape[1]
     hk = h // (Hq // Hkv)
     rows = np.asarray(list(rows), dtype=np.int64)
@@ -525,4 +527,4 @@ def attention_forward_fp8_rows(q8, k8, v8, q_descale: float, k_descale: float, v
         scale = default_scale(q8.shape[-1])
     q = dequantize_e4m3(q8[b, h], q_descale)[rows]
     return _head_attention(q, dequantize_e4m3(k8[b, hk], k_descale), dequantize_e4m3(v8[b, hk], v_descale),
-                           scale, causal, row_ids=rows)
+                           scale, causal, row_ids=rows, return_sp=return_sp)

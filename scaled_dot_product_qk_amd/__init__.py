@@ -20,10 +20,11 @@ ATTN_BF16, ATTN_F32 = 0, 1
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_DTYPE",
                 4: "ATTN_ERR_LAYOUT", 5: "ATTN_ERR_UNSUPPORTED", 6: "ATTN_ERR_WORKSPACE",
                 7: "ATTN_ERR_HIP"}
-EXPORTED = ("attn_fwd", "attn_fwd_masked", "attn_fwd_varlen", "attn_bwd", "attn_bwd_workspace_bytes",
-            "attn_decode", "attn_decode_workspace_bytes", "attn_validate_fwd", "attn_validate_fwd_masked",
-            "attn_validate_fwd_varlen", "attn_validate_bwd", "attn_validate_decode", "attn_status_str",
-            "attn_kernel_name", "attn_version")
+EXPORTED = ("attn_fwd", "attn_fwd_masked", "attn_fwd_varlen", "attn_fwd_fp8", "attn_bwd",
+            "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_workspace_bytes", "attn_validate_fwd",
+            "attn_validate_fwd_masked", "attn_validate_fwd_varlen", "attn_validate_fwd_fp8",
+            "attn_validate_bwd", "attn_validate_decode", "attn_status_str", "attn_kernel_name",
+            "attn_version")
 ATTN_MASK_BOOL, ATTN_MASK_ADD_BF16 = 1, 2
 
 _i64 = ctypes.c_int64
@@ -54,6 +55,16 @@ class FwdVarlenArgs(ctypes.Structure):
                 ("q_strides", _i64x2), ("k_strides", _i64x2), ("v_strides", _i64x2),
                 ("o_strides", _i64x2),
                 ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class FwdFp8Args(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("B", _i64), ("Hq", _i64), ("Hkv", _i64), ("Lq", _i64), ("Lk", _i64), ("d", _i64),
+                ("q_strides", _i64x3), ("k_strides", _i64x3), ("v_strides", _i64x3),
+                ("o_strides", _i64x3),
+                ("q_descale", ctypes.c_float), ("k_descale", ctypes.c_float), ("v_descale", ctypes.c_float),
+                ("causal", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
 class BwdArgs(ctypes.Structure):
@@ -105,6 +116,10 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_varlen.restype = ctypes.c_int
         L.attn_validate_fwd_varlen.argtypes = [ctypes.POINTER(FwdVarlenArgs)]
         L.attn_validate_fwd_varlen.restype = ctypes.c_int
+        L.attn_fwd_fp8.argtypes = [ctypes.POINTER(FwdFp8Args), ctypes.c_void_p]
+        L.attn_fwd_fp8.restype = ctypes.c_int
+        L.attn_validate_fwd_fp8.argtypes = [ctypes.POINTER(FwdFp8Args)]
+        L.attn_validate_fwd_fp8.restype = ctypes.c_int
         L.attn_bwd.argtypes = [ctypes.POINTER(BwdArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.attn_bwd.restype = ctypes.c_int
         L.attn_validate_bwd.argtypes = [ctypes.POINTER(BwdArgs)]
@@ -254,6 +269,51 @@ def attn_fwd_masked(q, k, v, mask, causal: bool = False, scale: Optional[float] 
     st = lib().attn_fwd_masked(ctypes.byref(args), ctypes.byref(margs), _stream_handle(stream))
     if st != 0:
         raise AttnError(st, "attn_fwd_masked")
+    return out, lse
+
+
+def make_fwd_fp8_args(q8, k8, v8, o, lse, descales, causal: bool, scale: Optional[float]) -> FwdFp8Args:
+    a = FwdFp8Args()
+    a.q, a.k, a.v, a.o, a.lse = q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), lse.data_ptr()
+    a.B, a.Hq, a.Lq, a.d = q8.shape
+    a.Hkv, a.Lk = k8.shape[1], k8.shape[2]
+    a.q_strides = _i64x3(*q8.stride()[:3])
+    a.k_strides = _i64x3(*k8.stride()[:3])
+    a.v_strides = _i64x3(*v8.stride()[:3])
+    a.o_strides = _i64x3(*o.stride()[:3])
+    a.q_descale, a.k_descale, a.v_descale = (float(x) for x in descales)
+    a.causal = 1 if causal else 0
+    a.scale = 0.0 if scale is None else float(scale)
+    return a
+
+
+def attn_fwd_fp8(q8, k8, v8, descales, causal: bool = False, scale: Optional[float] = None, out=None,
+                 lse=None, stream=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """O (bf16) and LSE of attention over e4m3 codes: q8 [B,Hq,Lq,d], k8/v8
+    [B,Hkv,Lk,d] as uint8 (or float8_e4m3fn) device tensors; descales =
+    (q_descale, k_descale, v_descale), an element standing for descale *
+    value(code)."""
+    import torch
+    q8, k8, v8 = (t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t for t in (q8, k8, v8))
+    _check_fwd_tensors(q8, k8, v8)
+    if q8.dtype != torch.uint8:
+        raise ValueError("q8, k8, v8 must hold e4m3 codes (torch.uint8 or torch.float8_e4m3fn)")
+    B, Hq, Lq, d = q8.shape
+    if out is None:
+        out = torch.empty((B, Hq, Lq, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q8.device)
+    _check_device(q8, out, lse)
+    if not lse.is_contiguous() or lse.dtype != torch.float32 or lse.shape != (B, Hq, Lq):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Lq] tensor")
+    if out.shape != q8.shape or out.dtype != torch.bfloat16 or (out.numel() and out.stride(3) != 1):
+        raise ValueError("out must be bf16 with q's shape and a contiguous head_dim")
+    if len(descales) != 3:
+        raise ValueError("descales = (q_descale, k_descale, v_descale)")
+    args = make_fwd_fp8_args(q8, k8, v8, out, lse, descales, causal, scale)
+    st = lib().attn_fwd_fp8(ctypes.byref(args), _stream_handle(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_fp8")
     return out, lse
 
 

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libattn_gfx950.so"
 SOURCES = ["attn_api.hip"]
-HEADERS = ["device_common.h", "fwd_bf16.h", "fwd_f32.h", "decode.h", "bwd_bf16.h"]
+HEADERS = ["device_common.h", "fwd_bf16.h", "fwd_f32.h", "fwd_fp8.h", "decode.h", "bwd_bf16.h"]
 
 
 def hipcc() -> str:

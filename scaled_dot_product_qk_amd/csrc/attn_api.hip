@@ -13,6 +13,7 @@
 #include "decode.h"
 #include "fwd_bf16.h"
 #include "fwd_f32.h"
+#include "fwd_fp8.h"
 
 using namespace attn_dev;
 
@@ -148,6 +149,7 @@ static FwdParams dense_fwd_params(const attn_fwd_args_t* a) {
   p.scale_log2_abs = std::fabs(p.scale_log2);
   p.inv_abs_scale = 1.0f / std::fabs(effective_scale(a->scale, a->d));
   p.neg_q = p.scale_log2 < 0.f ? 1 : 0;
+  p.o_mul = 1.f;
   return p;
 }
 
@@ -286,12 +288,97 @@ extern "C" attn_status_t attn_fwd_varlen(const attn_fwd_varlen_args_t* a, void* 
   p.scale_log2 = effective_scale(a->scale, a->d) * kLog2e;
   p.scale_log2_abs = std::fabs(p.scale_log2);
   p.neg_q = p.scale_log2 < 0.f ? 1 : 0;
+  p.o_mul = 1.f;
   const int grid_x = (int)(a->B * a->Hq);
   const bool c = a->causal != 0;
   switch (a->d) {
     case 64: return c ? launch_fwd_bf16<64, true>(p, grid_x, s) : launch_fwd_bf16<64, false>(p, grid_x, s);
     case 80: return c ? launch_fwd_bf16<80, true>(p, grid_x, s) : launch_fwd_bf16<80, false>(p, grid_x, s);
     case 128: return c ? launch_fwd_bf16<128, true>(p, grid_x, s) : launch_fwd_bf16<128, false>(p, grid_x, s);
+  }
+  return ATTN_ERR_UNSUPPORTED;
+}
+
+// ------------------------------------------------------------------ FP8
+extern "C" attn_status_t attn_validate_fwd_fp8(const attn_fwd_fp8_args_t* a) {
+  if (!a) return ATTN_ERR_NULL;
+  if (a->B < 0 || a->Hq < 0 || a->Hkv < 0 || a->Lq < 0 || a->Lk < 0 || a->d < 0) return ATTN_ERR_SHAPE;
+  if (!std::isfinite(a->scale) || !std::isfinite(a->q_descale) || !std::isfinite(a->k_descale) ||
+      !std::isfinite(a->v_descale))
+    return ATTN_ERR_SHAPE;
+  // the score multiplier scale * q_descale * k_descale * log2(e) must be a finite float
+  const double mult = (double)effective_scale(a->scale, a->d > 0 ? a->d : 1) * a->q_descale * a->k_descale * kLog2e;
+  if (!(std::fabs(mult) <= (double)std::numeric_limits<float>::max())) return ATTN_ERR_SHAPE;
+  if (a->d != 64 && a->d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (a->Hq > 0 && (a->Hkv == 0 || a->Hq % a->Hkv != 0)) return ATTN_ERR_SHAPE;
+  const bool work = a->B > 0 && a->Hq > 0 && a->Lq > 0;
+  if (!work) return ATTN_OK;
+  if (!a->q || !a->o || !a->lse) return ATTN_ERR_NULL;
+  if (a->Lk > 0 && (!a->k || !a->v)) return ATTN_ERR_NULL;
+  if (!aligned16(a->q) || !aligned16(a->o) || !aligned16(a->lse)) return ATTN_ERR_LAYOUT;
+  if (a->Lk > 0 && (!aligned16(a->k) || !aligned16(a->v))) return ATTN_ERR_LAYOUT;
+  if (!strides_ok(a->q_strides, 3, 1) || !strides_ok(a->k_strides, 3, 1) || !strides_ok(a->v_strides, 3, 1) ||
+      !strides_ok(a->o_strides, 3, 2))
+    return ATTN_ERR_LAYOUT;
+  if (a->Lq > kI32Max || a->Lk > kI32Max || a->B * a->Hq > kI32Max) return ATTN_ERR_UNSUPPORTED;
+  if (a->Lk > 0 &&
+      (a->k_strides[2] >= attn_dev::kFwdMaxTokenStride || a->v_strides[2] >= attn_dev::kFwdMaxTokenStride))
+    return ATTN_ERR_UNSUPPORTED;
+  if (a->B * a->Hq * ((a->Lq + 127) / 128) > kI32Max) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+template <int D, bool CAUSAL>
+static attn_status_t launch_fwd_fp8(const FwdParams& p, int grid_x, hipStream_t s) {
+  using S = Fp8FwdShape<D>;
+  constexpr int lds = S::kLdsBytes;
+  auto kern = attn_fwd_fp8_kernel<D, CAUSAL>;
+  static bool attr_set = false;  // racing first calls set the same value
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+      return ATTN_ERR_HIP;
+    attr_set = true;
+  }
+  FwdParams q = p;
+  q.n_qtiles = (p.Lq + S::kBR - 1) / S::kBR;
+  hipLaunchKernelGGL(kern, dim3(grid_x * q.n_qtiles), dim3(64 * S::kWaves), lds, s, q);
+  return launch_status();
+}
+
+extern "C" attn_status_t attn_fwd_fp8(const attn_fwd_fp8_args_t* a, void* stream) {
+  const attn_status_t st = attn_validate_fwd_fp8(a);
+  if (st != ATTN_OK) return st;
+  if (a->B == 0 || a->Hq == 0 || a->Lq == 0) return ATTN_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  FwdParams p;
+  p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->o; p.lse = a->lse;
+  p.q_sb = a->q_strides[0]; p.q_sh = a->q_strides[1]; p.q_st = a->q_strides[2];
+  p.k_sb = a->k_strides[0]; p.k_sh = a->k_strides[1]; p.k_st = a->k_strides[2];
+  p.v_sb = a->v_strides[0]; p.v_sh = a->v_strides[1]; p.v_st = a->v_strides[2];
+  p.o_sb = a->o_strides[0]; p.o_sh = a->o_strides[1]; p.o_st = a->o_strides[2];
+  p.Hq = (int)a->Hq;
+  p.Hkv = (int)a->Hkv;
+  p.group = (int)(a->Hq / a->Hkv);
+  p.Lq = (int)a->Lq;
+  p.Lk = (int)a->Lk;
+  p.n_qtiles = (int)((a->Lq + 127) / 128);
+  p.lse_sb = a->Hq * a->Lq;
+  p.lse_sh = a->Lq;
+  p.cu_q = nullptr;
+  p.cu_k = nullptr;
+  p.total_q = p.total_k = 0;
+  p.mask = nullptr;
+  p.m_sb = p.m_sh = p.m_sq = 0;
+  p.inv_abs_scale = 0.f;
+  p.scale_log2 = (float)((double)effective_scale(a->scale, a->d) * a->q_descale * a->k_descale * kLog2e);
+  p.scale_log2_abs = std::fabs(p.scale_log2);
+  p.neg_q = p.scale_log2 < 0.f ? 1 : 0;
+  p.o_mul = a->v_descale;
+  const int grid_x = (int)(a->B * a->Hq);
+  const bool c = a->causal != 0;
+  switch (a->d) {
+    case 64: return c ? launch_fwd_fp8<64, true>(p, grid_x, s) : launch_fwd_fp8<64, false>(p, grid_x, s);
+    case 128: return c ? launch_fwd_fp8<128, true>(p, grid_x, s) : launch_fwd_fp8<128, false>(p, grid_x, s);
   }
   return ATTN_ERR_UNSUPPORTED;
 }

@@ -69,6 +69,7 @@ struct FwdParams {
   float scale_log2;      // scale * log2(e)
   float scale_log2_abs;  // |scale * log2(e)|
   int neg_q;             // scale < 0: Q's sign bits are flipped on load (exact)
+  float o_mul;           // FP8 inputs: V's descale, applied to O with 1 / l
 };
 
 // Work-item order shared by the prefill kernels.  The hardware hands

@@ -344,3 +344,64 @@ def test_masked_rejections(fkw, kw, status):
 
 def test_masked_null_mask_struct():
     assert sdpa.lib().attn_validate_fwd_masked(ctypes.byref(fwd_args()), None) == NULL
+
+
+# ------------------------------------------------------------------ FP8
+def fp8_args(**kw):
+    a = sdpa.FwdFp8Args()
+    B, Hq, Hkv, Lq, Lk, d = kw.get("B", 2), kw.get("Hq", 8), kw.get("Hkv", 2), kw.get("Lq", 300), \
+        kw.get("Lk", 300), kw.get("d", 128)
+    a.q, a.k, a.v, a.o, a.lse = [kw.get(n, P + i * 0x10000000) for i, n in
+                                 enumerate(("q", "k", "v", "o", "lse"))]
+    a.B, a.Hq, a.Hkv, a.Lq, a.Lk, a.d = B, Hq, Hkv, Lq, Lk, d
+    a.q_strides = sdpa._i64x3(*kw.get("qs", (Hq * Lq * d, Lq * d, d)))
+    a.k_strides = sdpa._i64x3(*kw.get("ks", (Hkv * Lk * d, Lk * d, d)))
+    a.v_strides = sdpa._i64x3(*kw.get("vs", (Hkv * Lk * d, Lk * d, d)))
+    a.o_strides = sdpa._i64x3(*kw.get("os", (Hq * Lq * d, Lq * d, d)))
+    a.q_descale, a.k_descale, a.v_descale = kw.get("descales", (0.01, 0.02, 0.03))
+    a.causal = kw.get("causal", 0)
+    a.scale = kw.get("scale", 0.0)
+    return a
+
+
+def vfp8(**kw):
+    return sdpa.lib().attn_validate_fwd_fp8(ctypes.byref(fp8_args(**kw)))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("Lq,Lk", [(300, 300), (100, 700), (700, 100)])
+def test_fp8_valid(d, causal, Lq, Lk):
+    assert vfp8(d=d, causal=causal, Lq=Lq, Lk=Lk) == OK
+    assert vfp8(d=d, causal=causal, Lq=Lq, Lk=Lk, descales=(-0.5, 2.0, -1.0), scale=-0.1) == OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=80), UNSUP), (dict(d=96), UNSUP), (dict(Hq=6, Hkv=4), SHAPE), (dict(Lq=-1), SHAPE),
+    (dict(descales=(float("nan"), 1.0, 1.0)), SHAPE), (dict(descales=(1.0, float("inf"), 1.0)), SHAPE),
+    (dict(descales=(1.0, 1.0, float("inf"))), SHAPE), (dict(scale=float("nan")), SHAPE),
+    (dict(descales=(3e38, 3e38, 1.0)), SHAPE),                       # score multiplier past the float range
+    (dict(q=0), NULL), (dict(lse=0), NULL), (dict(k=0), NULL),
+    (dict(q=P + 8), LAYOUT), (dict(o=P + 4), LAYOUT),
+    (dict(qs=(300 * 8 * 128, 300 * 128, 136)), LAYOUT),              # token stride not 16 bytes
+    (dict(os=(300 * 8 * 128, 300 * 128, 132)), LAYOUT),              # bf16 output stride not 16 bytes
+    (dict(ks=(1 << 40, 1 << 30, 1 << 28)), UNSUP),                   # K token stride past 2^28 bytes
+])
+def test_fp8_rejections(kw, status):
+    assert vfp8(**kw) == status
+    a = fp8_args(**kw)
+    assert sdpa.lib().attn_fwd_fp8(ctypes.byref(a), None) == status
+
+
+def test_fp8_token_stride_limit_and_bf16_output_stride():
+    assert vfp8(ks=(1 << 40, 1 << 30, (1 << 28) - 16), vs=(1 << 40, 1 << 30, (1 << 28) - 16)) == OK
+    assert vfp8(os=(300 * 8 * 136, 300 * 136, 136)) == OK           # padded bf16 rows, 16-byte multiple
+
+
+def test_fp8_empty_inputs_are_valid_noops():
+    for kw in (dict(B=0), dict(Hq=0, Hkv=0), dict(Lq=0)):
+        a = fp8_args(q=0, k=0, v=0, o=0, lse=0, **kw)
+        assert sdpa.lib().attn_validate_fwd_fp8(ctypes.byref(a)) == OK
+        assert sdpa.lib().attn_fwd_fp8(ctypes.byref(a), None) == OK
+    assert vfp8(Lk=0, k=0, v=0) == OK
+    assert sdpa.lib().attn_validate_fwd_fp8(None) == NULL
