@@ -91,9 +91,28 @@ __device__ __forceinline__ WorkItem prefill_work_item(const FwdParams& p, bool c
   const int L = blockIdx.x;
   const int N = gridDim.x;
   if (p.cu_q != nullptr) {
-    // L = ((qi * B + b) * Hkv + hk) * group + hg, with N = n_qtiles * B * Hq
     const int nb = N / (p.n_qtiles * p.Hq);
     WorkItem it;
+    if ((p.Hkv & 7) == 0) {
+      // XCD x = L % 8 serves kv heads x, x + 8, ... of every sequence, so the
+      // XCDs carry equal work whatever the lengths; on one XCD the items go
+      // sequence by sequence (heaviest query tile first, the group's query
+      // heads together), so one sequence's K/V at a time lives in its L2.
+      // i = ((b * (Hkv / 8) + hkl) * n_qtiles + qi) * group + hg.
+      const int x = L & 7;
+      int i = L >> 3;
+      const int hg = i % p.group;
+      i /= p.group;
+      const int qi = i % p.n_qtiles;
+      i /= p.n_qtiles;
+      const int hpx = p.Hkv >> 3;
+      it.hk = (i % hpx) * 8 + x;
+      it.b = i / hpx;
+      it.h = it.hk * p.group + hg;
+      it.qt = causal ? p.n_qtiles - 1 - qi : qi;
+      return it;
+    }
+    // L = ((qi * B + b) * Hkv + hk) * group + hg, with N = n_qtiles * B * Hq
     const int hg = L % p.group;
     int r = L / p.group;
     it.hk = r % p.Hkv;
