@@ -281,8 +281,9 @@ attn_status_t attn_decode(const attn_decode_args_t *args, void *workspace,
                           size_t workspace_bytes, void *stream);
 
 /*
- * attn_bwd_workspace_bytes - bytes of device workspace attn_bwd needs (one
- * fp32 per query row: D = rowsum(dO * O)).  Returns 0 for invalid sizes.
+ * attn_bwd_workspace_bytes - bytes of device workspace attn_bwd needs (two
+ * fp32 per query row: LSE log2(e) and D = rowsum(dO * O)).  Returns 0 for
+ * invalid sizes.
  */
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq);
 
@@ -295,7 +296,8 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq);
  * memory of at least attn_bwd_workspace_bytes(B, Hq, Lq) bytes, 256-byte
  * aligned, contents irrelevant on entry.
  * Supported: dtype bf16; d in {64, 128}; Hq % Hkv == 0; Lq and Lk
- * independent; causal or not.  dK and dV of keys that no query sees are 0;
+ * independent; causal or not; Q and dO token strides below 2^26 elements
+ * (ATTN_ERR_UNSUPPORTED past it).  dK and dV of keys that no query sees are 0;
  * Lq == 0 gives dK = dV = 0.  B == 0, Hq == 0 or Lq == Lk == 0 is a no-op.
  */
 attn_status_t attn_bwd(const attn_bwd_args_t *args, void *workspace, size_t workspace_bytes,

@@ -388,7 +388,7 @@ bool bwd_head_dim_supported(int64_t d) { return d == 64 || d == 128; }
 
 extern "C" size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq) {
   if (B < 0 || Hq < 0 || Lq < 0) return 0;
-  return (size_t)((B * Hq * Lq * 4 + 255) / 256 * 256);
+  return (size_t)((B * Hq * Lq * 8 + 255) / 256 * 256);
 }
 
 extern "C" attn_status_t attn_validate_bwd(const attn_bwd_args_t* a) {
@@ -416,7 +416,25 @@ extern "C" attn_status_t attn_validate_bwd(const attn_bwd_args_t* a) {
     return ATTN_ERR_UNSUPPORTED;
   if (a->B * a->Hkv * ((a->Lk + 127) / 128) > kI32Max || a->B * a->Hq * ((a->Lq + 127) / 128) > kI32Max)
     return ATTN_ERR_UNSUPPORTED;
+  if (a->Lq > 0 && a->Lk > 0 &&
+      (a->q_strides[2] >= attn_dev::kBwdMaxTokenStride || a->do_strides[2] >= attn_dev::kBwdMaxTokenStride))
+    return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
+}
+
+template <int D, bool CAUSAL>
+static attn_status_t launch_bwd_dkdv(const BwdParams& p, int grid, hipStream_t s) {
+  using S = BwdKvShape<D>;
+  auto kern = attn_bwd_dkdv_kernel<D, CAUSAL>;
+  static bool attr_set = false;  // racing first calls set the same value
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, S::kLdsBytes) !=
+        hipSuccess)
+      return ATTN_ERR_HIP;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * S::kWaves), S::kLdsBytes, s, p);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 template <int D>
@@ -428,11 +446,8 @@ static attn_status_t launch_bwd(const BwdParams& p, bool causal, hipStream_t s) 
   }
   const int g_kv = p.B * p.Hkv * ((p.Lk + 127) / 128);
   if (g_kv > 0) {
-    if (causal)
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true>), dim3(g_kv), dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false>), dim3(g_kv), dim3(256), 0, s, p);
-    if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
+    const attn_status_t st = causal ? launch_bwd_dkdv<D, true>(p, g_kv, s) : launch_bwd_dkdv<D, false>(p, g_kv, s);
+    if (st != ATTN_OK) return st;
   }
   const int g_q = p.B * p.Hq * ((p.Lq + 127) / 128);
   if (g_q > 0) {
@@ -456,7 +471,7 @@ extern "C" attn_status_t attn_bwd(const attn_bwd_args_t* a, void* workspace, siz
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   BwdParams p;
   p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->o; p.dout = a->dout; p.lse = a->lse;
-  p.delta = reinterpret_cast<float*>(workspace);
+  p.stats = reinterpret_cast<float*>(workspace);
   p.dq = a->dq; p.dk = a->dk; p.dv = a->dv;
   p.q_sb = a->q_strides[0]; p.q_sh = a->q_strides[1]; p.q_st = a->q_strides[2];
   p.k_sb = a->k_strides[0]; p.k_sh = a->k_strides[1]; p.k_st = a->k_strides[2];

@@ -9,11 +9,12 @@
 // dQ = scale dS K, dK = scale dS^T Q.
 //
 // Three kernels:
-//   * attn_bwd_delta_kernel: D per query row (fp32, into the workspace);
+//   * attn_bwd_delta_kernel: per query row, (LSE log2 e, D) into the workspace;
 //   * attn_bwd_dkdv_kernel: one workgroup per (batch, kv head, 128 keys); each
-//     wave keeps its 32 keys' K and V in registers and walks the query heads of
-//     the group and their 32-query tiles (Q, dO, LSE and D staged in LDS), so
-//     dK and dV of a grouped head are summed without atomics;
+//     key group of 32 keeps its K and V in registers and walks the 32-query
+//     tiles of the group's query heads (Q, dO and the row statistics copied
+//     straight into LDS), so dK and dV of a grouped head are summed without
+//     atomics;
 //   * attn_bwd_dq_kernel: one workgroup per (batch, query head, 128 queries);
 //     each wave keeps its 32 queries' Q, dO, LSE and D in registers and walks
 //     32-key tiles of K and V staged in LDS.
@@ -42,7 +43,7 @@ struct BwdParams {
   const void* o;
   const void* dout;
   const float* lse;  // [B, Hq, Lq] from the forward
-  float* delta;      // workspace [B, Hq, Lq]
+  float* stats;      // workspace [B, Hq, Lq][2]: (LSE log2 e, D = rowsum(dO * O)) per query row
   void* dq;
   void* dk;
   void* dv;
@@ -90,7 +91,8 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc += bf16_lo(a[e]) * bf16_lo(d[e]) + bf16_hi(a[e]) * bf16_hi(d[e]);
   }
-  p.delta[row] = acc;
+  p.stats[2 * row] = p.lse[row] * kLog2e;
+  p.stats[2 * row + 1] = acc;
 }
 
 // Per-lane byte offset of the A operand X^T (32 head-dim rows of block db x 16
@@ -145,22 +147,65 @@ struct BwdTileLoader {
 };
 
 // ---------------------------------------------------------------- dK, dV
+// Largest Q / dO token stride (elements) the dK/dV kernel's copies allow: a
+// lane's 32-bit offset spans up to 31 rows of one 32-row tile.
+constexpr int64_t kBwdMaxTokenStride = int64_t(1) << 26;
+
+// dK/dV workgroup: 128 keys in 4 groups of 32; at head_dim 128 every group is
+// served by two waves that each own half of head_dim for dK and dV (and both
+// form the group's S and dP), so that a wave needs no more than 256
+// registers and two waves share each SIMD.  Q and dO tiles of 32 rows and
+// the rows' (LSE log2 e, D) pairs are copied straight into LDS, four steps in
+// flight.
+template <int D>
+struct BwdKvShape {
+  static constexpr int kSplit = D == 128 ? 2 : 1;
+  static constexpr int kWaves = 4 * kSplit;
+  static constexpr int kKC = D / 16;                  // k-slices over head_dim
+  static constexpr int kNDW = D / 32 / kSplit;        // 32-row head_dim blocks of dK^T, dV^T per wave
+  static constexpr int kChunks = D / 8;               // 16-byte chunks of a row
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kTileBytes = kBwdRows * kRowBytes;
+  static constexpr int kStatBytes = kBwdRows * 8;
+  static constexpr int kStageBytes = 2 * kTileBytes + kStatBytes;  // Q, dO, statistics
+  static constexpr int kStages = 4;
+  static constexpr int kLdsBytes = kStages * kStageBytes;
+  static constexpr int kRowsPerCopy = 1024 / kRowBytes;
+  static constexpr int kCopiesPerTile = kBwdRows / kRowsPerCopy;
+  static constexpr int kCopiesPerWave = 2 * kCopiesPerTile / kWaves;  // plus the statistics for wave 0
+  static_assert(kCopiesPerWave * kWaves == 2 * kCopiesPerTile, "copies split evenly over the waves");
+  static_assert(kCopiesPerTile % kCopiesPerWave == 0, "a wave copies from one tile only");
+};
+
+// LDS layout of a staged Q or dO row r: 16-byte chunk c at c ^ bwd_swz(r).
+// The rows are read two ways: 16 consecutive rows at one chunk (A operands of
+// S = Q K^T, dP = dO V^T) and, by the transposing read, 4 consecutive rows x
+// 2 (or 4) adjacent chunks per 16 (32) lanes; both hit distinct banks.
+//   256-byte rows: ((r & 3) << 2) | ((r >> 2) & 3);
+//   128-byte rows: (((r >> 1) & 1) << 2) | ((r >> 2) & 3).
+template <int D>
+__device__ __forceinline__ int bwd_swz(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void attn_bwd_dkdv_kernel(BwdParams p) {
-  using S = BwdShape<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t lq_tile[2][S::kTile];
-  __shared__ __attribute__((aligned(16))) uint16_t ldo_tile[2][S::kTile];
-  __shared__ __attribute__((aligned(16))) float lstat[2][2][kBwdRows];  // [buf][lse2, delta][row]
+__global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+  using S = BwdKvShape<D>;
+  typedef __attribute__((address_space(3))) char lds_char;
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds_raw[];
+  lds_char* const lds = (lds_char*)lds_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, ln = lane & 31;
-  const int n_kb = (p.Lk + 127) / 128;
-  const int kb = blockIdx.x % n_kb;
-  const int bh = blockIdx.x / n_kb;
+  const int kgrp = wave & 3, dpart = wave >> 2;
+  // Key blocks slowest (heaviest first when causal), (batch, kv head)
+  // fastest, so that the key blocks of one kv head run on one XCD.
+  const int n_bh = p.B * p.Hkv;
+  const int kb = blockIdx.x / n_bh, bh = blockIdx.x % n_bh;
   const int hk = bh % p.Hkv, b = bh / p.Hkv;
   const int k0 = kb * 128;
-  const int wave_k0 = k0 + 32 * wave;
+  const int wave_k0 = k0 + 32 * kgrp;
   const int key = wave_k0 + ln;  // this lane's key column
 
   // K^T and V^T as B operands of S = Q K^T and dP = dO V^T: lane holds row
@@ -176,91 +221,151 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void attn_bwd_dkdv_kernel(Bwd
       vop[kc] = ok ? load16(vr + 16 * kc + 8 * g) : zero16();
     }
   }
-  f32x16 dk_acc[S::kND], dv_acc[S::kND];
+  f32x16 dk_acc[S::kNDW], dv_acc[S::kNDW];
 #pragma unroll
-  for (int db = 0; db < S::kND; ++db)
+  for (int i = 0; i < S::kNDW; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dk_acc[db][r] = dv_acc[db][r] = 0.f;
+    for (int r = 0; r < 16; ++r) dk_acc[i][r] = dv_acc[i][r] = 0.f;
 
-  const int tr_off0 = bwd_tr_offset<D>(lane, 0);
+  // Steps: query tiles from the last down to the first one with a query at
+  // or after k0 (causal), the group's query heads within each tile, so that
+  // all key blocks of a kv head walk the same tiles at the same time.
   const int n_qt = (p.Lq + kBwdRows - 1) / kBwdRows;
-  const int qt0 = CAUSAL ? min(k0 / kBwdRows, n_qt) : 0;  // tiles before hold only queries < k0
-  const int tiles_per_head = n_qt - qt0;
-  const int n_steps = p.group * tiles_per_head;
+  const int qt_lo = CAUSAL ? min(k0 / kBwdRows, n_qt) : 0;
+  const int n_steps = p.group * (n_qt - qt_lo);
   const float c = p.scale_log2;
-  constexpr float kLog2eF = 1.4426950408889634f;
 
-  BwdTileLoader<D> lq_ld, ldo_ld;
-  float st_reg[2] = {0.f, 0.f};  // this thread's LSE (scaled to log2) and D, threads 0..31
-  auto load_step = [&](int step) {
-    const int hg = step / tiles_per_head, qt = qt0 + step % tiles_per_head;
+  // ---- copy plan: wave w issues copies kCopiesPerWave * w .. +kCopiesPerWave-1
+  // of a step (Q tile copies first, then dO); copy ci fills tile rows
+  // kRowsPerCopy * (ci % kCopiesPerTile) ..; lane -> row lane / kChunks,
+  // physical chunk lane % kChunks.  Wave 0 also copies the statistics.
+  const int ci0 = S::kCopiesPerWave * wave;
+  const bool cp_q = ci0 < S::kCopiesPerTile;
+  const int cp_row0 = S::kRowsPerCopy * (ci0 % S::kCopiesPerTile);
+  uint32_t cp_rel[S::kCopiesPerWave];   // byte offset of the lane's chunk within its row
+  int cp_row[S::kCopiesPerWave];        // tile row of the lane
+#pragma unroll
+  for (int j = 0; j < S::kCopiesPerWave; ++j) {
+    const int r = cp_row0 + S::kRowsPerCopy * j + lane / S::kChunks;
+    cp_row[j] = r;
+    cp_rel[j] = 16u * (uint32_t)((lane % S::kChunks) ^ bwd_swz<D>(r));
+  }
+  const int64_t cp_st = cp_q ? p.q_st : p.do_st;
+  const uint32_t cp_row_bytes = (uint32_t)(2 * cp_st);  // < 2^27: token strides are validated
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  auto issue_step = [&](int st) {
+    const int hg = st % p.group, qt = n_qt - 1 - st / p.group;
     const int h = hk * p.group + hg;
     const int r0 = qt * kBwdRows;
-    const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh;
-    const uint16_t* db = reinterpret_cast<const uint16_t*>(p.dout) + b * p.do_sb + h * p.do_sh;
-    lq_ld.load(qb, p.q_st, r0, p.Lq - 1, tid);
-    ldo_ld.load(db, p.do_st, r0, p.Lq - 1, tid);
-    if (tid < kBwdRows) {
-      const int64_t si = ((int64_t)b * p.Hq + h) * p.Lq + min(r0 + tid, p.Lq - 1);
-      st_reg[0] = p.lse[si] * kLog2eF;
-      st_reg[1] = p.delta[si];
+    const uint32_t dst = lds0 + (st % S::kStages) * S::kStageBytes + (cp_q ? 0 : S::kTileBytes);
+    const uint16_t* src = cp_q ? reinterpret_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh
+                               : reinterpret_cast<const uint16_t*>(p.dout) + b * p.do_sb + h * p.do_sh;
+    src += (int64_t)r0 * cp_st;
+#pragma unroll
+    for (int j = 0; j < S::kCopiesPerWave; ++j) {
+      const int row = min(r0 + cp_row[j], p.Lq - 1) - r0;  // rows past Lq repeat the last one
+      lds_copy16(src, (uint32_t)row * cp_row_bytes + cp_rel[j],
+                 dst + (cp_row0 + S::kRowsPerCopy * j) * S::kRowBytes);
+    }
+    if (wave == 0) {
+      const float* st_src = p.stats + 2 * (((int64_t)b * p.Hq + h) * p.Lq + r0);
+      const int row = min(r0 + (lane >> 1), p.Lq - 1) - r0;
+      lds_copy4(st_src, (uint32_t)(8 * row + 4 * (lane & 1)),
+                lds0 + (st % S::kStages) * S::kStageBytes + 2 * S::kTileBytes);
     }
   };
-  auto store_step = [&](int buf) {
-    lq_ld.store(lq_tile[buf], tid);
-    ldo_ld.store(ldo_tile[buf], tid);
-    if (tid < kBwdRows) {
-      lstat[buf][0][tid] = st_reg[0];
-      lstat[buf][1][tid] = st_reg[1];
+  // Waits until at most `pending` later steps' copies of this wave are in flight.
+  auto wait_steps = [&](int pending) {
+    if (wave == 0) {
+      constexpr int n = S::kCopiesPerWave + 1;
+      if (pending >= 2) __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * n));
+      else if (pending == 1) __builtin_amdgcn_s_waitcnt(0x0f70 | n);
+      else __builtin_amdgcn_s_waitcnt(0x0f70);
+    } else {
+      constexpr int n = S::kCopiesPerWave;
+      if (pending >= 2) __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * n));
+      else if (pending == 1) __builtin_amdgcn_s_waitcnt(0x0f70 | n);
+      else __builtin_amdgcn_s_waitcnt(0x0f70);
     }
   };
 
-  if (n_steps > 0) {
-    load_step(0);
-    store_step(0);
+  // ---- LDS operand offsets within a tile ----
+  // Row reads (A operands of S and dP): row ln, chunk 2 kc + g.
+  const int rd_off = ln * S::kRowBytes + 16 * (g ^ bwd_swz<D>(ln));
+  // Transposing reads (A operands X^T of dV^T, dK^T): lane (G, i, q) points at
+  // row 16 cs + 4 g + i (+8), head-dim 32 db + 16 (G & 1) + 4 q; the chunk is
+  // 4 db + 2 (G & 1) + q / 2, so block db is block 0's offset with 64 db
+  // XOR-ed in.
+  int tr_off[2];
+  {
+    const int G = lane >> 4, i = (lane & 15) >> 2, q = lane & 3;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int r = 4 * g + i + 8 * hh;
+      tr_off[hh] = r * S::kRowBytes + 16 * ((2 * (G & 1) + (q >> 1)) ^ bwd_swz<D>(r)) + 8 * (q & 1);
+    }
   }
+  auto tr_read = [&](const lds_char* tile, int db, int cs) {
+    typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+    const lds_char* t = tile + 16 * cs * S::kRowBytes;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(t + (tr_off[0] ^ (64 * db))));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(t + (tr_off[1] ^ (64 * db))));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    const uint32_t a0 = l2[0], a1 = l2[1], a2 = h2[0], a3 = h2[1];
+    return u32x4{a0, a1, a2, a3};
+  };
+
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): K and V have landed before the copies start
+#pragma unroll
+  for (int st = 0; st < S::kStages - 1; ++st)
+    if (st < n_steps) issue_step(st);
+
   for (int step = 0; step < n_steps; ++step) {
-    const int buf = step & 1;
-    if (step + 1 < n_steps) load_step(step + 1);
-    __syncthreads();
-    const int qt = qt0 + step % tiles_per_head;
+    wait_steps(min(S::kStages - 2, n_steps - 1 - step));
+    __syncthreads();  // step's tiles in LDS; every wave is done with step - 1's buffer
+    if (step + S::kStages - 1 < n_steps) issue_step(step + S::kStages - 1);
+    const int qt = n_qt - 1 - step / p.group;
     const int r0 = qt * kBwdRows;
     // A wave whose keys all come after the tile's last query has nothing here.
     if (!CAUSAL || r0 + kBwdRows - 1 >= wave_k0) {
-      const uint16_t* qt_l = lq_tile[buf];
-      const uint16_t* dt_l = ldo_tile[buf];
+      const lds_char* qt_l = lds + (step % S::kStages) * S::kStageBytes;
+      const lds_char* dt_l = qt_l + S::kTileBytes;
+      const float* st_l = (const float*)(qt_l + 2 * S::kTileBytes);
       // S = Q K^T and dP = dO V^T: rows = the tile's 32 queries, columns = keys.
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
       for (int kc = 0; kc < S::kKC; ++kc) {
-        const u32x4 qa = *reinterpret_cast<const u32x4*>(qt_l + ln * S::kPitch + 16 * kc + 8 * g);
-        const u32x4 da = *reinterpret_cast<const u32x4*>(dt_l + ln * S::kPitch + 16 * kc + 8 * g);
+        const u32x4 qa = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(qt_l + (rd_off ^ (32 * kc)));
+        const u32x4 da = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(dt_l + (rd_off ^ (32 * kc)));
         s = mfma32(qa, kop[kc], s);
         dp = mfma32(da, vop[kc], dp);
       }
-      // The row statistics of this lane's 16 query rows 8 j + 4 g + 0..3.
-      f32x4 lse4[4], dl4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        lse4[j] = *reinterpret_cast<const f32x4*>(&lstat[buf][0][8 * j + 4 * g]);
-        dl4[j] = *reinterpret_cast<const f32x4*>(&lstat[buf][1][8 * j + 4 * g]);
-      }
-      // P = exp2(c S - LSE log2 e) (recomputed), dS = P (dP - D); both packed
-      // as the B operands of the two 16-query slices.
+      // P = exp2(c S - LSE log2 e), dS = P (dP - D), packed as the B operands
+      // of the two 16-query slices; rows 8 (r / 4) + 4 g + r % 4.
       u32x4 pb[2], dsb[2];
 #pragma unroll
       for (int cs = 0; cs < 2; ++cs) {
         float pe[8], de[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * cs + e;
-          const int qrow = r0 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool vis = qrow < p.Lq && key < p.Lk && (!CAUSAL || key <= qrow);
-          const float pv = vis ? fast_exp2(__builtin_fmaf(s[r], c, -lse4[r >> 2][r & 3])) : 0.f;
-          pe[e] = pv;
-          de[e] = pv * (dp[r] - dl4[r >> 2][r & 3]);
+        for (int jj = 0; jj < 2; ++jj) {
+          const int rb = 8 * (2 * cs + jj) + 4 * g;  // first of 4 consecutive rows
+          const f32x4 s01 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+              (const lds_char*)st_l + 8 * rb);
+          const f32x4 s23 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+              (const lds_char*)st_l + 8 * rb + 16);
+          const float l2v[4] = {s01[0], s01[2], s23[0], s23[2]};
+          const float dlv[4] = {s01[1], s01[3], s23[1], s23[3]};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 8 * cs + 4 * jj + e;
+            const int qrow = r0 + rb + e;
+            const bool vis = qrow < p.Lq && key < p.Lk && (!CAUSAL || key <= qrow);
+            const float pv = vis ? fast_exp2(__builtin_fmaf(s[r], c, -l2v[e])) : 0.f;
+            pe[4 * jj + e] = pv;
+            de[4 * jj + e] = pv * (dp[r] - dlv[e]);
+          }
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -268,19 +373,16 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void attn_bwd_dkdv_kernel(Bwd
           dsb[cs][j] = pack_bf16x2(de[2 * j], de[2 * j + 1]);
         }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS (rows = head_dim, columns = keys).
+      // dV^T += dO^T P and dK^T += Q^T dS over this wave's head_dim blocks.
 #pragma unroll
-      for (int db = 0; db < S::kND; ++db)
+      for (int i = 0; i < S::kNDW; ++i)
 #pragma unroll
         for (int cs = 0; cs < 2; ++cs) {
-          const u32x4 dta = bwd_tr_read<D>(reinterpret_cast<const char*>(dt_l), tr_off0 + 64 * db, cs);
-          const u32x4 qta = bwd_tr_read<D>(reinterpret_cast<const char*>(qt_l), tr_off0 + 64 * db, cs);
-          dv_acc[db] = mfma32(dta, pb[cs], dv_acc[db]);
-          dk_acc[db] = mfma32(qta, dsb[cs], dk_acc[db]);
+          const int db = dpart * S::kNDW + i;
+          dv_acc[i] = mfma32(tr_read(dt_l, db, cs), pb[cs], dv_acc[i]);
+          dk_acc[i] = mfma32(tr_read(qt_l, db, cs), dsb[cs], dk_acc[i]);
         }
     }
-    // The other buffer was last read before this iteration's barrier.
-    if (step + 1 < n_steps) store_step(buf ^ 1);
   }
 
   // dK = scale dK_acc, dV = dV_acc: lane = key, registers = head-dim rows.
@@ -288,15 +390,15 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void attn_bwd_dkdv_kernel(Bwd
     uint16_t* dkr = reinterpret_cast<uint16_t*>(p.dk) + b * p.dk_sb + hk * p.dk_sh + (int64_t)key * p.dk_st;
     uint16_t* dvr = reinterpret_cast<uint16_t*>(p.dv) + b * p.dv_sb + hk * p.dv_sh + (int64_t)key * p.dv_st;
 #pragma unroll
-    for (int db = 0; db < S::kND; ++db)
+    for (int i = 0; i < S::kNDW; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int d = 32 * db + 8 * j + 4 * g;
+        const int d = 32 * (dpart * S::kNDW + i) + 8 * j + 4 * g;
         u32x2 wk, wv;
-        wk[0] = pack_bf16x2(dk_acc[db][4 * j + 0] * p.scale, dk_acc[db][4 * j + 1] * p.scale);
-        wk[1] = pack_bf16x2(dk_acc[db][4 * j + 2] * p.scale, dk_acc[db][4 * j + 3] * p.scale);
-        wv[0] = pack_bf16x2(dv_acc[db][4 * j + 0], dv_acc[db][4 * j + 1]);
-        wv[1] = pack_bf16x2(dv_acc[db][4 * j + 2], dv_acc[db][4 * j + 3]);
+        wk[0] = pack_bf16x2(dk_acc[i][4 * j + 0] * p.scale, dk_acc[i][4 * j + 1] * p.scale);
+        wk[1] = pack_bf16x2(dk_acc[i][4 * j + 2] * p.scale, dk_acc[i][4 * j + 3] * p.scale);
+        wv[0] = pack_bf16x2(dv_acc[i][4 * j + 0], dv_acc[i][4 * j + 1]);
+        wv[1] = pack_bf16x2(dv_acc[i][4 * j + 2], dv_acc[i][4 * j + 3]);
         *reinterpret_cast<u32x2*>(dkr + d) = wk;
         *reinterpret_cast<u32x2*>(dvr + d) = wv;
       }
@@ -335,10 +437,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
       dop[kc] = qok ? load16(dr + 16 * kc + 8 * g) : zero16();
     }
   }
-  constexpr float kLog2eF = 1.4426950408889634f;
   const int64_t si = ((int64_t)b * p.Hq + h) * p.Lq + min(qrow, p.Lq - 1);
-  const float lse2 = qok ? p.lse[si] * kLog2eF : 0.f;
-  const float dl = qok ? p.delta[si] : 0.f;
+  const float lse2 = qok ? p.stats[2 * si] : 0.f;
+  const float dl = qok ? p.stats[2 * si + 1] : 0.f;
   const float c = p.scale_log2;
 
   f32x16 dq_acc[S::kND];

@@ -83,6 +83,19 @@ __device__ __forceinline__ float sum_xor16(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Copies from global memory straight into LDS, 16 (or 4) bytes per lane:
+// from base + off (base wave-uniform, off a per-lane byte offset) to lds_base
+// + 16 * lane (+ 4 * lane), lds_base wave-uniform.  Inline assembly, so that
+// the compiler neither counts the copies among its outstanding loads nor makes
+// LDS reads and barriers wait for them: kernels wait for their own copies
+// (vmcnt) before the barrier that publishes them.
+__device__ __forceinline__ void lds_copy16(const void* base, uint32_t off, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_base) : "memory");
+}
+__device__ __forceinline__ void lds_copy4(const void* base, uint32_t off, uint32_t lds_base) {
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_base) : "memory");
+}
+
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

@@ -212,14 +212,8 @@ __device__ __forceinline__ int fwd_v_swz(int r) {
   return (PITCH / 4) * (r & 3);
 }
 
-// 16 bytes per lane from global memory at base + off (base wave-uniform, off
-// a per-lane byte offset) into LDS at lds_base + 16 * lane (lds_base
-// wave-uniform).  Inline assembly, so that the compiler neither counts the
-// copy among its outstanding loads nor makes LDS reads and barriers wait for
-// it: the kernel waits for its copies itself (vmcnt) before the barrier that
-// publishes them.
 __device__ __forceinline__ void fwd_copy16(const void* base, uint32_t off, uint32_t lds_base) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_base) : "memory");
+  lds_copy16(base, off, lds_base);
 }
 
 // Largest K/V token stride (elements) the copies' 32-bit lane offsets allow:

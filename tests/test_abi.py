@@ -296,7 +296,7 @@ def test_bwd_rejections(kw, status):
 def test_bwd_workspace_rules():
     L = sdpa.lib()
     need = sdpa.attn_bwd_workspace_bytes(2, 8, 300)
-    assert need == (2 * 8 * 300 * 4 + 255) // 256 * 256
+    assert need == (2 * 8 * 300 * 8 + 255) // 256 * 256
     assert L.attn_bwd(ctypes.byref(bwd_args()), None, need, None) == WS
     assert L.attn_bwd(ctypes.byref(bwd_args()), P, need - 1, None) == WS
     assert L.attn_bwd(ctypes.byref(bwd_args()), P + 16, need, None) == LAYOUT
@@ -305,6 +305,14 @@ def test_bwd_workspace_rules():
     assert L.attn_bwd(ctypes.byref(bwd_args(B=0)), None, 0, None) == OK
     assert L.attn_bwd(ctypes.byref(bwd_args(Lq=0, Lk=0)), None, 0, None) == OK
     assert L.attn_validate_bwd(None) == NULL
+
+
+def test_bwd_query_token_stride_limit():
+    # the dK/dV kernel's copies address up to 31 rows of Q and dO with 32-bit lane offsets
+    big = 1 << 26
+    assert vbwd(Lq=300, Lk=300, qs=(8 * big * 300, big * 300, big)) == UNSUP
+    assert vbwd(Lq=300, Lk=300, dos=(8 * big * 300, big * 300, big)) == UNSUP
+    assert vbwd(Lq=300, Lk=300, qs=(8 * (big - 8) * 300, (big - 8) * 300, big - 8)) == OK
 
 
 def mask_args(**kw):
