@@ -417,7 +417,8 @@ extern "C" attn_status_t attn_validate_bwd(const attn_bwd_args_t* a) {
   if (a->B * a->Hkv * ((a->Lk + 127) / 128) > kI32Max || a->B * a->Hq * ((a->Lq + 127) / 128) > kI32Max)
     return ATTN_ERR_UNSUPPORTED;
   if (a->Lq > 0 && a->Lk > 0 &&
-      (a->q_strides[2] >= attn_dev::kBwdMaxTokenStride || a->do_strides[2] >= attn_dev::kBwdMaxTokenStride))
+      (a->q_strides[2] >= attn_dev::kBwdMaxTokenStride || a->do_strides[2] >= attn_dev::kBwdMaxTokenStride ||
+       a->k_strides[2] >= attn_dev::kBwdMaxTokenStride || a->v_strides[2] >= attn_dev::kBwdMaxTokenStride))
     return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
@@ -426,6 +427,21 @@ template <int D, bool CAUSAL>
 static attn_status_t launch_bwd_dkdv(const BwdParams& p, int grid, hipStream_t s) {
   using S = BwdKvShape<D>;
   auto kern = attn_bwd_dkdv_kernel<D, CAUSAL>;
+  static bool attr_set = false;  // racing first calls set the same value
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, S::kLdsBytes) !=
+        hipSuccess)
+      return ATTN_ERR_HIP;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * S::kWaves), S::kLdsBytes, s, p);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+template <int D, bool CAUSAL>
+static attn_status_t launch_bwd_dq(const BwdParams& p, int grid, hipStream_t s) {
+  using S = BwdQShape<D>;
+  auto kern = attn_bwd_dq_kernel<D, CAUSAL>;
   static bool attr_set = false;  // racing first calls set the same value
   if (!attr_set) {
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, S::kLdsBytes) !=
@@ -451,11 +467,8 @@ static attn_status_t launch_bwd(const BwdParams& p, bool causal, hipStream_t s) 
   }
   const int g_q = p.B * p.Hq * ((p.Lq + 127) / 128);
   if (g_q > 0) {
-    if (causal)
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<D, true>), dim3(g_q), dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<D, false>), dim3(g_q), dim3(256), 0, s, p);
-    if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
+    const attn_status_t st = causal ? launch_bwd_dq<D, true>(p, g_q, s) : launch_bwd_dq<D, false>(p, g_q, s);
+    if (st != ATTN_OK) return st;
   }
   return ATTN_OK;
 }

@@ -17,7 +17,7 @@
 //     atomics;
 //   * attn_bwd_dq_kernel: one workgroup per (batch, query head, 128 queries);
 //     each wave keeps its 32 queries' Q, dO, LSE and D in registers and walks
-//     32-key tiles of K and V staged in LDS.
+//     32-key tiles of K and V copied straight into LDS.
 // Both products of a tile that contract over its rows (dV^T += dO^T P,
 // dK^T += Q^T dS, dQ^T += K^T dS^T) take their A operand from the transposing
 // LDS read ds_read_b64_tr_b16 on the row-major tile, visiting the rows in the
@@ -62,17 +62,6 @@ struct BwdParams {
 
 constexpr int kBwdRows = 32;  // rows of a staged tile (queries or keys)
 
-template <int D>
-struct BwdShape {
-  static constexpr int kKC = D / 16;     // k-slices over head_dim
-  static constexpr int kND = D / 32;     // 32-row blocks of a transposed gradient
-  static constexpr int kPitch = D + 8;   // row pitch in LDS (elements): 16-byte rows, spread banks
-  static constexpr int kTile = kBwdRows * kPitch;       // elements of one staged tile
-  static constexpr int kChunks = kBwdRows * D / 8;      // 16-byte chunks of one tile
-  static constexpr int kIter = (kChunks + 255) / 256;   // per thread, per tensor
-  static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
-};
-
 // ---------------------------------------------------------------- delta
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
@@ -95,59 +84,8 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
   p.stats[2 * row + 1] = acc;
 }
 
-// Per-lane byte offset of the A operand X^T (32 head-dim rows of block db x 16
-// tile rows of slice cs) read with ds_read_b64_tr_b16 from a row-major tile:
-// lane (G = l/16, i = l%16/4, q = l%4) points at tile row 16 cs + 4 g + i,
-// head-dim 32 db + 16 (G & 1) + 4 q; the second read is 8 rows further.
-template <int D>
-__device__ __forceinline__ int bwd_tr_offset(int lane, int db) {
-  using S = BwdShape<D>;
-  const int g = lane >> 5, G = lane >> 4, i = (lane & 15) >> 2, q = lane & 3;
-  return ((4 * g + i) * S::kPitch + 32 * db + 16 * (G & 1) + 4 * q) * 2;
-}
-
-template <int D>
-__device__ __forceinline__ u32x4 bwd_tr_read(const char* tile, int off, int cs) {
-  typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
-  using S = BwdShape<D>;
-  const char* a0 = tile + off + 16 * cs * S::kPitch * 2;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) const char*)a0);
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) const char*)(a0 + 8 * S::kPitch * 2));
-  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-  return u32x4{l2[0], l2[1], h2[0], h2[1]};
-}
-
-// Stage rows r0 .. r0+31 (clamped to last) of a [rows, D] tensor into a tile.
-template <int D>
-struct BwdTileLoader {
-  using S = BwdShape<D>;
-  u32x4 reg[S::kIter];
-  __device__ __forceinline__ void load(const uint16_t* base, int64_t st, int r0, int last, int tid) {
-#pragma unroll
-    for (int it = 0; it < S::kIter; ++it) {
-      const int c = tid + 256 * it;
-      if (S::kChunks % 256 == 0 || c < S::kChunks) {
-        const int row = c / (D / 8), ch = c % (D / 8);
-        reg[it] = load16(base + (int64_t)min(r0 + row, last) * st + 8 * ch);
-      }
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* tile, int tid) const {
-#pragma unroll
-    for (int it = 0; it < S::kIter; ++it) {
-      const int c = tid + 256 * it;
-      if (S::kChunks % 256 == 0 || c < S::kChunks) {
-        const int row = c / (D / 8), ch = c % (D / 8);
-        *reinterpret_cast<u32x4*>(tile + row * S::kPitch + 8 * ch) = reg[it];
-      }
-    }
-  }
-};
-
 // ---------------------------------------------------------------- dK, dV
-// Largest Q / dO token stride (elements) the dK/dV kernel's copies allow: a
+// Largest Q, dO, K, V token stride (elements) the backward's copies allow: a
 // lane's 32-bit offset spans up to 31 rows of one 32-row tile.
 constexpr int64_t kBwdMaxTokenStride = int64_t(1) << 26;
 
@@ -406,19 +344,57 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
 }
 
 // ---------------------------------------------------------------- dQ
+// dQ workgroup: 4 waves x 32 queries of one (batch, query head); 32-key tiles
+// of K and V copied straight into LDS (the dK/dV kernel's swizzle: K is read
+// by rows and transposed), four steps in flight.
+template <int D>
+struct BwdQShape {
+  static constexpr int kWaves = 4;
+  static constexpr int kKC = D / 16;
+  static constexpr int kND = D / 32;
+  static constexpr int kChunks = D / 8;
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kTileBytes = kBwdRows * kRowBytes;
+  static constexpr int kStageBytes = 2 * kTileBytes;  // K, V
+  static constexpr int kStages = 4;
+  static constexpr int kLdsBytes = kStages * kStageBytes;
+  static constexpr int kRowsPerCopy = 1024 / kRowBytes;
+  static constexpr int kCopiesPerTile = kBwdRows / kRowsPerCopy;
+  static constexpr int kCopiesPerWave = 2 * kCopiesPerTile / kWaves;
+  static_assert(kCopiesPerWave * kWaves == 2 * kCopiesPerTile, "copies split evenly over the waves");
+  static_assert(kCopiesPerTile % kCopiesPerWave == 0, "a wave copies from one tile only");
+  static_assert(2 * kCopiesPerWave < 16, "the wait counts fit the simple vmcnt encoding");
+};
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
-  using S = BwdShape<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t lk_tile[2][S::kTile];
-  __shared__ __attribute__((aligned(16))) uint16_t lv_tile[2][S::kTile];
+  using S = BwdQShape<D>;
+  typedef __attribute__((address_space(3))) char lds_char;
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds_raw[];
+  lds_char* const lds = (lds_char*)lds_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, ln = lane & 31;
+  // Work order as in the forward: each XCD receives one contiguous range of
+  // work items ordered (batch, kv head, query block, query head of the
+  // group), heaviest query blocks first when causal, so the workgroups that
+  // re-read one kv head's K and V share an L2.
   const int n_qb = (p.Lq + 127) / 128;
-  const int qb = blockIdx.x % n_qb;
-  const int bh = blockIdx.x / n_qb;
-  const int h = bh % p.Hq, b = bh / p.Hq;
+  int h, b, qb;
+  {
+    const int L = blockIdx.x, N = gridDim.x;
+    const int full = N & ~7;
+    const int w = L < full ? (L & 7) * (full >> 3) + (L >> 3) : L;
+    const int hg = w % p.group;
+    int r = w / p.group;
+    const int qi = r % n_qb;
+    r /= n_qb;
+    const int hk = r % p.Hkv;
+    b = r / p.Hkv;
+    h = hk * p.group + hg;
+    qb = CAUSAL ? n_qb - 1 - qi : qi;
+  }
   const int hk = h / p.group;
   const int q0 = qb * 128;
   const int wave_q0 = q0 + 32 * wave;
@@ -450,36 +426,73 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
 
   int n_kt = (p.Lk + kBwdRows - 1) / kBwdRows;
   if (CAUSAL) n_kt = min(n_kt, (q0 + 127) / kBwdRows + 1);
-  const int tr_off0 = bwd_tr_offset<D>(lane, 0);
-  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(p.k) + b * p.k_sb + hk * p.k_sh;
-  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(p.v) + b * p.v_sb + hk * p.v_sh;
-  BwdTileLoader<D> lk_ld, lv_ld;
 
-  if (n_kt > 0) {
-    lk_ld.load(kbase, p.k_st, 0, p.Lk - 1, tid);
-    lv_ld.load(vbase, p.v_st, 0, p.Lk - 1, tid);
-    lk_ld.store(lk_tile[0], tid);
-    lv_ld.store(lv_tile[0], tid);
+  // ---- copy plan: waves 0-1 copy the K tile, waves 2-3 the V tile ----
+  const int ci0 = S::kCopiesPerWave * wave;
+  const bool cp_k = ci0 < S::kCopiesPerTile;
+  const int cp_row0 = S::kRowsPerCopy * (ci0 % S::kCopiesPerTile);
+  uint32_t cp_rel[S::kCopiesPerWave];
+  int cp_row[S::kCopiesPerWave];
+#pragma unroll
+  for (int j = 0; j < S::kCopiesPerWave; ++j) {
+    const int r = cp_row0 + S::kRowsPerCopy * j + lane / S::kChunks;
+    cp_row[j] = r;
+    cp_rel[j] = 16u * (uint32_t)((lane % S::kChunks) ^ bwd_swz<D>(r));
   }
-  for (int t = 0; t < n_kt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_kt) {
-      lk_ld.load(kbase, p.k_st, (t + 1) * kBwdRows, p.Lk - 1, tid);
-      lv_ld.load(vbase, p.v_st, (t + 1) * kBwdRows, p.Lk - 1, tid);
+  const int64_t cp_st = cp_k ? p.k_st : p.v_st;
+  const uint32_t cp_row_bytes = (uint32_t)(2 * cp_st);  // < 2^27: token strides are validated
+  const uint16_t* cp_base = cp_k ? reinterpret_cast<const uint16_t*>(p.k) + b * p.k_sb + hk * p.k_sh
+                                 : reinterpret_cast<const uint16_t*>(p.v) + b * p.v_sb + hk * p.v_sh;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  auto issue_step = [&](int t) {
+    const int r0 = t * kBwdRows;
+    const uint32_t dst = lds0 + (t % S::kStages) * S::kStageBytes + (cp_k ? 0 : S::kTileBytes);
+    const uint16_t* src = cp_base + (int64_t)r0 * cp_st;
+#pragma unroll
+    for (int j = 0; j < S::kCopiesPerWave; ++j) {
+      const int row = min(r0 + cp_row[j], p.Lk - 1) - r0;  // keys past Lk repeat the last one
+      lds_copy16(src, (uint32_t)row * cp_row_bytes + cp_rel[j], dst + (cp_row0 + S::kRowsPerCopy * j) * S::kRowBytes);
     }
+  };
+  auto wait_steps = [&](int pending) {
+    constexpr int n = S::kCopiesPerWave;
+    if (pending >= 2) __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * n));
+    else if (pending == 1) __builtin_amdgcn_s_waitcnt(0x0f70 | n);
+    else __builtin_amdgcn_s_waitcnt(0x0f70);
+  };
+
+  const int rd_off = ln * S::kRowBytes + 16 * (g ^ bwd_swz<D>(ln));
+  int tr_off[2];
+  {
+    const int G = lane >> 4, i = (lane & 15) >> 2, q = lane & 3;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int r = 4 * g + i + 8 * hh;
+      tr_off[hh] = r * S::kRowBytes + 16 * ((2 * (G & 1) + (q >> 1)) ^ bwd_swz<D>(r)) + 8 * (q & 1);
+    }
+  }
+
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): Q, dO and the statistics have landed
+#pragma unroll
+  for (int t = 0; t < S::kStages - 1; ++t)
+    if (t < n_kt) issue_step(t);
+
+  for (int t = 0; t < n_kt; ++t) {
+    wait_steps(min(S::kStages - 2, n_kt - 1 - t));
     __syncthreads();
+    if (t + S::kStages - 1 < n_kt) issue_step(t + S::kStages - 1);
     const int kv0 = t * kBwdRows;
     if (!CAUSAL || kv0 <= wave_q0 + 31) {
-      const uint16_t* kt_l = lk_tile[buf];
-      const uint16_t* vt_l = lv_tile[buf];
+      const lds_char* kt_l = lds + (t % S::kStages) * S::kStageBytes;
+      const lds_char* vt_l = kt_l + S::kTileBytes;
       // S^T = K Q^T and dP^T = V dO^T: rows = the tile's 32 keys, columns = queries.
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
       for (int kc = 0; kc < S::kKC; ++kc) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(kt_l + ln * S::kPitch + 16 * kc + 8 * g);
-        const u32x4 va = *reinterpret_cast<const u32x4*>(vt_l + ln * S::kPitch + 16 * kc + 8 * g);
+        const u32x4 ka = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(kt_l + (rd_off ^ (32 * kc)));
+        const u32x4 va = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(vt_l + (rd_off ^ (32 * kc)));
         s = mfma32(ka, qop[kc], s);
         dp = mfma32(va, dop[kc], dp);
       }
@@ -504,14 +517,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int db = 0; db < S::kND; ++db)
 #pragma unroll
-        for (int cs = 0; cs < 2; ++cs)
-          dq_acc[db] = mfma32(bwd_tr_read<D>(reinterpret_cast<const char*>(kt_l), tr_off0 + 64 * db, cs), dsb[cs],
-                              dq_acc[db]);
-    }
-    // The other buffer was last read before this iteration's barrier.
-    if (t + 1 < n_kt) {
-      lk_ld.store(lk_tile[buf ^ 1], tid);
-      lv_ld.store(lv_tile[buf ^ 1], tid);
+        for (int cs = 0; cs < 2; ++cs) {
+          typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+          const lds_char* tt = kt_l + 16 * cs * S::kRowBytes;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(tt + (tr_off[0] ^ (64 * db))));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(tt + (tr_off[1] ^ (64 * db))));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+          const uint32_t a0 = l2[0], a1 = l2[1], a2 = h2[0], a3 = h2[1];
+          dq_acc[db] = mfma32(u32x4{a0, a1, a2, a3}, dsb[cs], dq_acc[db]);
+        }
     }
   }
 

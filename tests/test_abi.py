@@ -308,10 +308,12 @@ def test_bwd_workspace_rules():
 
 
 def test_bwd_query_token_stride_limit():
-    # the dK/dV kernel's copies address up to 31 rows of Q and dO with 32-bit lane offsets
+    # the backward's copies address up to 31 rows of Q, dO, K and V with 32-bit lane offsets
     big = 1 << 26
     assert vbwd(Lq=300, Lk=300, qs=(8 * big * 300, big * 300, big)) == UNSUP
     assert vbwd(Lq=300, Lk=300, dos=(8 * big * 300, big * 300, big)) == UNSUP
+    assert vbwd(Lq=300, Lk=300, ks=(2 * big * 300, big * 300, big)) == UNSUP
+    assert vbwd(Lq=300, Lk=300, vs=(2 * big * 300, big * 300, big)) == UNSUP
     assert vbwd(Lq=300, Lk=300, qs=(8 * (big - 8) * 300, (big - 8) * 300, big - 8)) == OK
 
 
