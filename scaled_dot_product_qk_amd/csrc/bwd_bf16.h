@@ -246,8 +246,9 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
   auto tr_read = [&](const lds_char* tile, int db, int cs) {
     typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
     const lds_char* t = tile + 16 * cs * S::kRowBytes;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(t + (tr_off[0] ^ (64 * db))));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(t + (tr_off[1] ^ (64 * db))));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + (tr_off[0] ^ (64 * db))));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + (tr_off[1] ^ (64 * db))));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
     const uint32_t a0 = l2[0], a1 = l2[1], a2 = h2[0], a3 = h2[1];
     return u32x4{a0, a1, a2, a3};

@@ -26,8 +26,9 @@
 //
 // Causal (top-left: query i sees keys j <= i, for any Lq and Lk): key tiles
 // entirely above a wave's last row are skipped; tiles that straddle the
-// diagonal or the end of the keys are masked to -inf.  Key tile 0 is processed first and holds a visible key for every
-// row, so the reference max is finite after each row's first tile.
+// diagonal or the end of the keys are masked to -inf.  Key tile 0 is
+// processed first and holds a visible key for every row, so the reference max
+// is finite after each row's first tile.
 #pragma once
 
 #include <type_traits>
@@ -142,9 +143,6 @@ __device__ __forceinline__ WorkItem prefill_work_item(const FwdParams& p, bool c
 // from LDS then feeds two matrix instructions), one at larger head_dims where
 // the output accumulator alone would not leave room for two waves per SIMD.
 __host__ __device__ constexpr int bf16_fwd_blocks_per_wave(int d) { return d <= 64 ? 2 : 1; }
-__host__ __device__ constexpr int bf16_fwd_rows_per_workgroup(int d) {
-  return 4 * 32 * bf16_fwd_blocks_per_wave(d);
-}
 
 template <int D>
 struct Bf16FwdShape {
