@@ -295,7 +295,7 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq);
  * atomics, so results are deterministic.  `workspace` is caller-owned device
  * memory of at least attn_bwd_workspace_bytes(B, Hq, Lq) bytes, 256-byte
  * aligned, contents irrelevant on entry.
- * Supported: dtype bf16; d in {64, 128}; Hq % Hkv == 0; Lq and Lk
+ * Supported: dtype bf16; d in {64, 80, 128}; Hq % Hkv == 0; Lq and Lk
  * independent; causal or not; Q, dO, K and V token strides below 2^26 elements
  * (ATTN_ERR_UNSUPPORTED past it).  dK and dV of keys that no query sees are 0;
  * Lq == 0 gives dK = dV = 0.  B == 0, Hq == 0 or Lq == Lk == 0 is a no-op.

@@ -384,7 +384,7 @@ extern "C" attn_status_t attn_fwd_fp8(const attn_fwd_fp8_args_t* a, void* stream
 }
 
 // ------------------------------------------------------------------ backward
-bool bwd_head_dim_supported(int64_t d) { return d == 64 || d == 128; }
+bool bwd_head_dim_supported(int64_t d) { return d == 64 || d == 80 || d == 128; }
 
 extern "C" size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq) {
   if (B < 0 || Hq < 0 || Lq < 0) return 0;
@@ -505,6 +505,7 @@ extern "C" attn_status_t attn_bwd(const attn_bwd_args_t* a, void* workspace, siz
   const bool c = a->causal != 0;
   switch (a->d) {
     case 64: return launch_bwd<64>(p, c, s);
+    case 80: return launch_bwd<80>(p, c, s);
     case 128: return launch_bwd<128>(p, c, s);
   }
   return ATTN_ERR_UNSUPPORTED;

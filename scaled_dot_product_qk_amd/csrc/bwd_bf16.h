@@ -100,9 +100,11 @@ struct BwdKvShape {
   static constexpr int kSplit = D == 128 ? 2 : 1;
   static constexpr int kWaves = 4 * kSplit;
   static constexpr int kKC = D / 16;                  // k-slices over head_dim
-  static constexpr int kNDW = D / 32 / kSplit;        // 32-row head_dim blocks of dK^T, dV^T per wave
-  static constexpr int kChunks = D / 8;               // 16-byte chunks of a row
-  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kND = (D + 31) / 32;           // 32-row head_dim blocks (the last padded at d = 80)
+  static constexpr int kNDW = kND / kSplit;           // ... per wave
+  static constexpr int kChunks = D / 8;               // 16-byte chunks of a row in memory
+  static constexpr int kPitch = D <= 64 ? 8 : 16;     // 16-byte chunks of a row in LDS
+  static constexpr int kRowBytes = 16 * kPitch;
   static constexpr int kTileBytes = kBwdRows * kRowBytes;
   static constexpr int kStatBytes = kBwdRows * 8;
   static constexpr int kStageBytes = 2 * kTileBytes + kStatBytes;  // Q, dO, statistics
@@ -113,6 +115,7 @@ struct BwdKvShape {
   static constexpr int kCopiesPerWave = 2 * kCopiesPerTile / kWaves;  // plus the statistics for wave 0
   static_assert(kCopiesPerWave * kWaves == 2 * kCopiesPerTile, "copies split evenly over the waves");
   static_assert(kCopiesPerTile % kCopiesPerWave == 0, "a wave copies from one tile only");
+  static_assert(kND % kSplit == 0 && kChunks <= kPitch, "head_dim blocks split evenly; rows fit their pitch");
 };
 
 // LDS layout of a staged Q or dO row r: 16-byte chunk c at c ^ bwd_swz(r).
@@ -121,9 +124,10 @@ struct BwdKvShape {
 // 2 (or 4) adjacent chunks per 16 (32) lanes; both hit distinct banks.
 //   256-byte rows: ((r & 3) << 2) | ((r >> 2) & 3);
 //   128-byte rows: (((r >> 1) & 1) << 2) | ((r >> 2) & 3).
-template <int D>
+// Head_dim 80 rows (10 chunks) take 256-byte rows; chunks 10-15 are padding.
+template <int PITCH>
 __device__ __forceinline__ int bwd_swz(int r) {
-  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  return PITCH == 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 template <int D, bool CAUSAL>
@@ -175,18 +179,20 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
 
   // ---- copy plan: wave w issues copies kCopiesPerWave * w .. +kCopiesPerWave-1
   // of a step (Q tile copies first, then dO); copy ci fills tile rows
-  // kRowsPerCopy * (ci % kCopiesPerTile) ..; lane -> row lane / kChunks,
-  // physical chunk lane % kChunks.  Wave 0 also copies the statistics.
+  // kRowsPerCopy * (ci % kCopiesPerTile) ..; lane -> row lane / kPitch,
+  // physical chunk lane % kPitch.  Wave 0 also copies the statistics.
   const int ci0 = S::kCopiesPerWave * wave;
   const bool cp_q = ci0 < S::kCopiesPerTile;
   const int cp_row0 = S::kRowsPerCopy * (ci0 % S::kCopiesPerTile);
   uint32_t cp_rel[S::kCopiesPerWave];   // byte offset of the lane's chunk within its row
   int cp_row[S::kCopiesPerWave];        // tile row of the lane
+  int cp_lc[S::kCopiesPerWave];         // slots of padding chunks (head_dim 80) stay idle
 #pragma unroll
   for (int j = 0; j < S::kCopiesPerWave; ++j) {
-    const int r = cp_row0 + S::kRowsPerCopy * j + lane / S::kChunks;
+    const int r = cp_row0 + S::kRowsPerCopy * j + lane / S::kPitch;
     cp_row[j] = r;
-    cp_rel[j] = 16u * (uint32_t)((lane % S::kChunks) ^ bwd_swz<D>(r));
+    cp_lc[j] = (lane % S::kPitch) ^ bwd_swz<S::kPitch>(r);  // logical chunk of the lane's slot
+    cp_rel[j] = 16u * (uint32_t)cp_lc[j];
   }
   const int64_t cp_st = cp_q ? p.q_st : p.do_st;
   const uint32_t cp_row_bytes = (uint32_t)(2 * cp_st);  // < 2^27: token strides are validated
@@ -202,8 +208,9 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
 #pragma unroll
     for (int j = 0; j < S::kCopiesPerWave; ++j) {
       const int row = min(r0 + cp_row[j], p.Lq - 1) - r0;  // rows past Lq repeat the last one
-      lds_copy16(src, (uint32_t)row * cp_row_bytes + cp_rel[j],
-                 dst + (cp_row0 + S::kRowsPerCopy * j) * S::kRowBytes);
+      if (S::kChunks == S::kPitch || cp_lc[j] < S::kChunks)
+        lds_copy16(src, (uint32_t)row * cp_row_bytes + cp_rel[j],
+                   dst + (cp_row0 + S::kRowsPerCopy * j) * S::kRowBytes);
     }
     if (wave == 0) {
       const float* st_src = p.stats + 2 * (((int64_t)b * p.Hq + h) * p.Lq + r0);
@@ -229,7 +236,7 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
 
   // ---- LDS operand offsets within a tile ----
   // Row reads (A operands of S and dP): row ln, chunk 2 kc + g.
-  const int rd_off = ln * S::kRowBytes + 16 * (g ^ bwd_swz<D>(ln));
+  const int rd_off = ln * S::kRowBytes + 16 * (g ^ bwd_swz<S::kPitch>(ln));
   // Transposing reads (A operands X^T of dV^T, dK^T): lane (G, i, q) points at
   // row 16 cs + 4 g + i (+8), head-dim 32 db + 16 (G & 1) + 4 q; the chunk is
   // 4 db + 2 (G & 1) + q / 2, so block db is block 0's offset with 64 db
@@ -240,7 +247,7 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int r = 4 * g + i + 8 * hh;
-      tr_off[hh] = r * S::kRowBytes + 16 * ((2 * (G & 1) + (q >> 1)) ^ bwd_swz<D>(r)) + 8 * (q & 1);
+      tr_off[hh] = r * S::kRowBytes + 16 * ((2 * (G & 1) + (q >> 1)) ^ bwd_swz<S::kPitch>(r)) + 8 * (q & 1);
     }
   }
   auto tr_read = [&](const lds_char* tile, int db, int cs) {
@@ -333,6 +340,7 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * (dpart * S::kNDW + i) + 8 * j + 4 * g;
+        if (d >= D) continue;  // padding rows of the last block (head_dim 80)
         u32x2 wk, wv;
         wk[0] = pack_bf16x2(dk_acc[i][4 * j + 0] * p.scale, dk_acc[i][4 * j + 1] * p.scale);
         wk[1] = pack_bf16x2(dk_acc[i][4 * j + 2] * p.scale, dk_acc[i][4 * j + 3] * p.scale);
@@ -352,9 +360,10 @@ template <int D>
 struct BwdQShape {
   static constexpr int kWaves = 4;
   static constexpr int kKC = D / 16;
-  static constexpr int kND = D / 32;
+  static constexpr int kND = (D + 31) / 32;           // the last block padded at d = 80
   static constexpr int kChunks = D / 8;
-  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kPitch = D <= 64 ? 8 : 16;     // 16-byte chunks of a row in LDS
+  static constexpr int kRowBytes = 16 * kPitch;
   static constexpr int kTileBytes = kBwdRows * kRowBytes;
   static constexpr int kStageBytes = 2 * kTileBytes;  // K, V
   static constexpr int kStages = 4;
@@ -365,6 +374,7 @@ struct BwdQShape {
   static_assert(kCopiesPerWave * kWaves == 2 * kCopiesPerTile, "copies split evenly over the waves");
   static_assert(kCopiesPerTile % kCopiesPerWave == 0, "a wave copies from one tile only");
   static_assert(2 * kCopiesPerWave < 16, "the wait counts fit the simple vmcnt encoding");
+  static_assert(kChunks <= kPitch, "rows fit their pitch");
 };
 
 template <int D, bool CAUSAL>
@@ -434,11 +444,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   const int cp_row0 = S::kRowsPerCopy * (ci0 % S::kCopiesPerTile);
   uint32_t cp_rel[S::kCopiesPerWave];
   int cp_row[S::kCopiesPerWave];
+  int cp_lc[S::kCopiesPerWave];
 #pragma unroll
   for (int j = 0; j < S::kCopiesPerWave; ++j) {
-    const int r = cp_row0 + S::kRowsPerCopy * j + lane / S::kChunks;
+    const int r = cp_row0 + S::kRowsPerCopy * j + lane / S::kPitch;
     cp_row[j] = r;
-    cp_rel[j] = 16u * (uint32_t)((lane % S::kChunks) ^ bwd_swz<D>(r));
+    cp_lc[j] = (lane % S::kPitch) ^ bwd_swz<S::kPitch>(r);  // logical chunk of the lane's slot
+    cp_rel[j] = 16u * (uint32_t)cp_lc[j];
   }
   const int64_t cp_st = cp_k ? p.k_st : p.v_st;
   const uint32_t cp_row_bytes = (uint32_t)(2 * cp_st);  // < 2^27: token strides are validated
@@ -452,7 +464,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int j = 0; j < S::kCopiesPerWave; ++j) {
       const int row = min(r0 + cp_row[j], p.Lk - 1) - r0;  // keys past Lk repeat the last one
-      lds_copy16(src, (uint32_t)row * cp_row_bytes + cp_rel[j], dst + (cp_row0 + S::kRowsPerCopy * j) * S::kRowBytes);
+      if (S::kChunks == S::kPitch || cp_lc[j] < S::kChunks)
+        lds_copy16(src, (uint32_t)row * cp_row_bytes + cp_rel[j],
+                   dst + (cp_row0 + S::kRowsPerCopy * j) * S::kRowBytes);
     }
   };
   auto wait_steps = [&](int pending) {
@@ -462,14 +476,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
     else __builtin_amdgcn_s_waitcnt(0x0f70);
   };
 
-  const int rd_off = ln * S::kRowBytes + 16 * (g ^ bwd_swz<D>(ln));
+  const int rd_off = ln * S::kRowBytes + 16 * (g ^ bwd_swz<S::kPitch>(ln));
   int tr_off[2];
   {
     const int G = lane >> 4, i = (lane & 15) >> 2, q = lane & 3;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int r = 4 * g + i + 8 * hh;
-      tr_off[hh] = r * S::kRowBytes + 16 * ((2 * (G & 1) + (q >> 1)) ^ bwd_swz<D>(r)) + 8 * (q & 1);
+      tr_off[hh] = r * S::kRowBytes + 16 * ((2 * (G & 1) + (q >> 1)) ^ bwd_swz<S::kPitch>(r)) + 8 * (q & 1);
     }
   }
 
@@ -539,6 +553,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * db + 8 * j + 4 * g;
+        if (d >= D) continue;  // padding rows of the last block (head_dim 80)
         u32x2 w;
         w[0] = pack_bf16x2(dq_acc[db][4 * j + 0] * p.scale, dq_acc[db][4 * j + 1] * p.scale);
         w[1] = pack_bf16x2(dq_acc[db][4 * j + 2] * p.scale, dq_acc[db][4 * j + 3] * p.scale);

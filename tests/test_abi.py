@@ -274,7 +274,7 @@ def vbwd(**kw):
     return sdpa.lib().attn_validate_bwd(ctypes.byref(bwd_args(**kw)))
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 80, 128])
 @pytest.mark.parametrize("causal", [0, 1])
 @pytest.mark.parametrize("Lq,Lk", [(300, 300), (100, 700), (700, 100)])
 def test_bwd_valid(d, causal, Lq, Lk):
@@ -283,7 +283,7 @@ def test_bwd_valid(d, causal, Lq, Lk):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=0), NULL), (dict(dout=0), NULL), (dict(lse=0), NULL), (dict(dq=0), NULL), (dict(dk=0), NULL),
-    (dict(dv=0), NULL), (dict(dtype=1), UNSUP), (dict(dtype=9), DTYPE), (dict(d=80), UNSUP), (dict(d=96), UNSUP),
+    (dict(dv=0), NULL), (dict(dtype=1), UNSUP), (dict(dtype=9), DTYPE), (dict(d=96), UNSUP), (dict(d=32), UNSUP),
     (dict(Hkv=3), SHAPE), (dict(Lq=-1), SHAPE), (dict(scale=float("nan")), SHAPE),
     (dict(dq=P + 8), LAYOUT), (dict(lse=P + 2), LAYOUT), (dict(dos=(8 * 300 * 64, 300 * 64, 66)), LAYOUT),
 ])

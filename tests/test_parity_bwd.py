@@ -67,7 +67,7 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 80, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", SHAPES)
 def test_bwd_small(dev, d, causal, shape):
@@ -134,3 +134,20 @@ def test_workload_bwd_causal_gqa_n8192_sampled(dev):
         grad_check("dq", dq[0, hk * g:(hk + 1) * g][:, rows], sq, f"C4 bwd kv head {hk}")
         grad_check("dk", dk[0, hk, keys], sk, f"C4 bwd kv head {hk}")
         grad_check("dv", dv[0, hk, keys], sv, f"C4 bwd kv head {hk}")
+
+
+def test_workload_bwd_causal_d80_sampled(dev):
+    """The causal d=80 workload (B=4, H=16, n=2048): head_dim 80 rows sit in
+    256-byte LDS rows and the last 32-row head_dim block is half padding;
+    sampled query rows and keys of two (batch, head) pairs."""
+    w = wl.C3
+    q, k, v, do = inputs(w, w.seed + 50)
+    dq, dk, dv = run_gpu(q, k, v, do, dev, True)
+    dq, dk, dv = to_np(dq), to_np(dk), to_np(dv)
+    rows = [0, 1, 31, 32, 1023, 2047]
+    keys = [0, 31, 32, 1024, 2046, 2047]
+    for b, h in ((0, 0), (3, 15)):
+        sq, sk, sv = orc.attention_backward_sampled(q, k, v, do, b, h, rows, keys, causal=True)
+        grad_check("dq", dq[b, h:h + 1][:, rows], sq, f"C3 bwd b{b} h{h}")
+        grad_check("dk", dk[b, h, keys], sk, f"C3 bwd b{b} h{h}")
+        grad_check("dv", dv[b, h, keys], sv, f"C3 bwd b{b} h{h}")
