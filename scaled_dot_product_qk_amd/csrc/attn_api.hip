@@ -95,7 +95,7 @@ static attn_status_t launch_status() {
 
 template <int D, bool CAUSAL, int MK = 0>
 static attn_status_t launch_fwd_bf16(const FwdParams& p, int grid_x, hipStream_t s) {
-  constexpr int lds = Bf16FwdShape<D>::kLdsBytes + FwdMaskShape<D, MK>::kLdsBytes;
+  constexpr int lds = FwdMaskShape<D, CAUSAL, MK>::kKernelLdsBytes;
   auto kern = attn_fwd_bf16_kernel<D, CAUSAL, MK>;
   static bool attr_set = false;  // racing first calls set the same value
   if (!attr_set) {

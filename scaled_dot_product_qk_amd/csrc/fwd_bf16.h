@@ -10,7 +10,8 @@
 // Work decomposition: one workgroup of 4 waves per (batch, query head, tile
 // of query rows); wave w owns 64 rows at head_dim 64 and 32 rows otherwise.
 // Key/value tiles of 64 keys are copied from global memory straight into LDS,
-// double buffered, and shared by the 4 waves.
+// double buffered (three buffers for the pipelined schedule below), and
+// shared by the 4 waves.
 //
 // Orientation: every product is taken transposed, S^T = K Q^T and
 // O^T = V^T P^T, so that in both the score accumulator and the output
@@ -160,7 +161,6 @@ struct Bf16FwdShape {
   static constexpr int kRowBytes = 16 * kPitch;
   static constexpr int kTileBytes = kBC * kRowBytes;
   static constexpr int kBufBytes = 2 * kTileBytes;  // K tile, then V tile
-  static constexpr int kLdsBytes = 2 * kBufBytes;   // double buffered
   static constexpr int kRowsPerCopy = 64 / kPitch;  // rows one 1 KB copy instruction fills
   static constexpr int kCopies = 2 * kBC / kRowsPerCopy;  // per tile, K then V
   static constexpr int kCopiesPerWave = kCopies / kWaves;
@@ -172,10 +172,19 @@ struct Bf16FwdShape {
   static_assert(kBufBytes < 65536, "in-buffer LDS offsets must fit the instruction offset field");
 };
 
+// Key/value tile buffers in LDS: three for the pipelined schedule (head_dim
+// 64, not causal, no mask; there a tile's V operands are read after the
+// barrier at which the copies of the tile two ahead are issued), two
+// otherwise.  (The causal instance would need more than 256 registers per
+// lane for the pipeline: its diagonal tiles' masking spills Q's operands.)
+__host__ __device__ constexpr int bf16_fwd_kv_stages(int d, bool causal, int mk) {
+  return d == 64 && !causal && mk == 0 ? 3 : 2;
+}
+
 // Attention-mask tiles (MK: 1 uint8 boolean, 2 bf16 additive): the
 // workgroup's query rows x the 64 keys of a tile, row-major, double buffered
 // after the key/value buffers, copied with the key/value tiles.
-template <int D, int MK>
+template <int D, bool CAUSAL, int MK>
 struct FwdMaskShape {
   using S = Bf16FwdShape<D>;
   static_assert(S::kCopiesPerWave + (MK == 0 ? 0 : S::kBR / (1024 / (S::kBC * (MK == 1 ? 1 : 2))) / S::kWaves) < 16,
@@ -190,6 +199,9 @@ struct FwdMaskShape {
   static constexpr int kCopiesPerWave = kCopies / S::kWaves;
   static constexpr int kLdsBytes = MK == 0 ? 0 : 2 * kTileBytes;
   static_assert(MK == 0 || kCopies % S::kWaves == 0, "mask copies split evenly over the waves");
+  // dynamic LDS of the kernel: key/value buffers, then the mask tiles
+  static constexpr int kKVBytes = bf16_fwd_kv_stages(D, CAUSAL, MK) * S::kBufBytes;
+  static constexpr int kKernelLdsBytes = kKVBytes + kLdsBytes;
 };
 
 // LDS layout of a key row: its 16-byte chunks are XOR-swizzled by the row
@@ -234,8 +246,10 @@ template <int D, bool CAUSAL, int MK = 0>
 __global__ __launch_bounds__(64 * Bf16FwdShape<D>::kWaves, Bf16FwdShape<D>::kGroupsPerCU) void
 attn_fwd_bf16_kernel(FwdParams p_in) {
   using S = Bf16FwdShape<D>;
-  using MS = FwdMaskShape<D, MK>;
+  using MS = FwdMaskShape<D, CAUSAL, MK>;
   constexpr int NB = S::kNB;
+  constexpr int kStages = bf16_fwd_kv_stages(D, CAUSAL, MK);
+  constexpr bool kPipe = kStages == 3;  // the pipelined schedule
   typedef __attribute__((address_space(3))) char lds_char;
   typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -340,14 +354,14 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
     m_lrow = lane / MS::kChunksPerRow;
     m_chunk = lane % MS::kChunksPerRow;
     m_row0 = wave * MS::kCopiesPerWave * MS::kRowsPerCopy;
-    m_lds0 = (uint32_t)(uintptr_t)lds_b + S::kLdsBytes;
+    m_lds0 = (uint32_t)(uintptr_t)lds_b + MS::kKVBytes;
   }
   // Full tiles copy without checks; the tile holding key Lk - 1 reads rows
   // beyond it from row Lk - 1 instead (in bounds and finite), and those keys
   // are masked to -inf, so they carry weight 0.
-  auto issue_tile = [&](int t) {
+  auto issue_tile = [&](int t, int buf) __attribute__((always_inline)) {
     const int kv0 = t * S::kBC;
-    const uint32_t dst = cp_lds0 + (t & 1) * S::kBufBytes;
+    const uint32_t dst = cp_lds0 + buf * S::kBufBytes;
     if (t < n_full) {
 #pragma unroll
       for (int j = 0; j < S::kCopiesPerWave; ++j) {
@@ -418,30 +432,71 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
     l_run[nb] = 0.f;
   }
 
-  // One key tile: S^T, online softmax, O^T += V^T P^T.  MASK selects the
-  // variant that masks keys beyond Lk and (causal) keys after the query.
+  // Key tiles are taken as two 32-key halves, each with its own sum guard
+  // (the probabilities of a half depend only on its own scores and the
+  // reference max, see kSumGuard), so that the products of one half can run
+  // on the matrix core while the vector ALU forms the softmax of another.
   //
-  // The tile is taken as two 32-key halves so that each wave keeps its matrix
-  // core and its vector ALU busy at once: the products of one half are issued
-  // interleaved with the softmax of the other,
+  // Head_dim 64, not causal, no mask (kPipe): a software pipeline across
+  // tiles.  With S(t, h) the scores of half h of tile t and PV(t, h) its
+  // O^T += V^T P^T products,
   //
-  //   S(h0) | S(h1) + softmax(h0) | O += P(h0) V(h0) + softmax(h1) | O += P(h1) V(h1)
+  //   phase A of tile t:  PV(t-1, 1) + S(t, 1)    beside softmax(t, 0)
+  //   (wait for tile t+1, barrier, copy tile t+2, read K of tile t+1)
+  //   phase B of tile t:  PV(t, 0)   + S(t+1, 0)  beside softmax(t, 1)
   //
-  // which is possible because the probabilities of a half depend only on its
-  // own scores and the reference max (see kSumGuard): each half has its own
-  // guard, and a rescale of O after the first half's products is exact.
-  // tile_front runs all but the last products; the K operands of the first
-  // half come from ka_next, read ahead while the previous tile's last
-  // products ran (tile_back).
+  // so every softmax half runs beside 16 products.  A rescale of O in
+  // softmax(t, h) follows, in program order, the products of every earlier
+  // half (their probabilities were formed against the old reference), so it
+  // scales them too and stays exact.  The second half's V^T operands are
+  // read at the end of phase B, after the barrier of tile t: with three LDS
+  // buffers, tile t's buffer is refilled only after the barrier of tile t + 1.
+  //
+  // The other instances (head_dim 80 and 128, causal, masked) keep both
+  // softmax halves of a tile before its barrier, which needs fewer registers
+  // and, with a mask, keeps the mask words of the tile readable from LDS:
+  //
+  //   S(t, 0) | S(t, 1) + softmax(t, 0) | PV(t, 0) + softmax(t, 1) | barrier | PV(t, 1)
   u32x4 ka_next[S::kKC];     // K operands, first key half of the next tile
+  u32x4 ka1[S::kKC];         // K operands, second key half of this tile
+  u32x4 va0[S::kND][2];      // V^T operands, first key half of this tile
   u32x4 va_last[S::kND][2];  // V^T operands, second key half of this tile
   u32x4 pop[NB][4];          // P^T B operands, one per 16-key slice
+  f32x16 s[NB][2];           // S^T accumulators, one per key half
+  // (the buffer's byte offset goes through readfirstlane so that it stays one
+  // scalar term of the address and the constant parts fold into the
+  // instructions' offset fields)
+  auto buf_bytes = [&](int buf) { return __builtin_amdgcn_readfirstlane(buf * S::kBufBytes); };
   auto read_k = [&](int buf, int sb, u32x4 (&ka)[S::kKC]) {
-    const lds_char* kb = lds_b + buf * S::kBufBytes;
+    const lds_char* kb = lds_b + buf_bytes(buf);
 #pragma unroll
     for (int kc = 0; kc < S::kKC; ++kc)
       ka[kc] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
           kb + (k_rd ^ (32 * kc)) + 32 * sb * S::kRowBytes);
+  };
+  auto read_v = [&](int buf, int sb, u32x4 (&va)[S::kND][2]) {
+    lds_char* vb = lds_b + buf_bytes(buf);
+#pragma unroll
+    for (int db = 0; db < S::kND; ++db)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        lds_char* a0 = vb + v_rd[db] + 16 * (2 * sb + j) * S::kRowBytes;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)a0);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(a0 + 8 * S::kRowBytes));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        va[db][j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+      }
+  };
+  auto qk = [&](int sb, const u32x4 (&ka)[S::kKC]) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[nb][sb][r] = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < S::kKC; ++kc)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) s[nb][sb] = mfma32(ka[kc], qop[nb][kc], s[nb][sb]);
   };
   auto pv = [&](int sb, const u32x4 (&va)[S::kND][2]) {
 #pragma unroll
@@ -451,187 +506,234 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) oacc[nb][db] = mfma32(va[db][j], pop[nb][2 * sb + j], oacc[nb][db]);
   };
-  auto tile_back = [&] {
-    __builtin_amdgcn_s_setprio(2);
-    pv(1, va_last);
-    __builtin_amdgcn_s_setprio(0);
+  // P = exp2(c s - m) for half sb of row block nb, packed as two P^T B
+  // operands; returns this lane's share of the half's row sum.
+  auto exp_half = [&](int sb, int nb) __attribute__((always_inline)) {
+    // (with an attention mask a row may still have no visible key: its
+    // reference stays -inf and every probability is exp2(-inf) = 0)
+    const float neg_m = (MK != 0 && m_run[nb] == kNegInf) ? 0.f : -m_run[nb];
+    // four short dependency chains, each started by its first value (an
+    // explicit 0 + e is an instruction: the compiler keeps it for signed zeros)
+    float rs[4];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        e[i] = fast_exp2(__builtin_fmaf(s[nb][sb][8 * half + i], c, neg_m));
+        if (half == 0 && i < 4)
+          rs[i] = e[i];
+        else
+          rs[i & 3] += e[i];
+      }
+      u32x4 pk;
+      pk[0] = pack_bf16x2(e[0], e[1]);
+      pk[1] = pack_bf16x2(e[2], e[3]);
+      pk[2] = pack_bf16x2(e[4], e[5]);
+      pk[3] = pack_bf16x2(e[6], e[7]);
+      pop[nb][2 * sb + half] = pk;
+    }
+    return (rs[0] + rs[1]) + (rs[2] + rs[3]);
   };
-  auto tile_front = [&](auto mask_tag, int buf, int kv0) {
+  // Softmax of half sb of the tile in buffer buf starting at key kv0; MASK
+  // selects the variant that masks keys beyond Lk and (causal) keys after the
+  // query.  N_MFMA products issued just before it are spread between its
+  // vector instructions.
+  auto softmax_half = [&](auto mask_tag, int buf, int kv0, int sb, auto n_mfma_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    lds_char* vb = lds_b + buf * S::kBufBytes;
-    f32x16 s[NB][2];
-    auto read_v = [&](int sb, u32x4 (&va)[S::kND][2]) {
-#pragma unroll
-      for (int db = 0; db < S::kND; ++db)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          lds_char* a0 = vb + v_rd[db] + 16 * (2 * sb + j) * S::kRowBytes;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)a0);
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(a0 + 8 * S::kRowBytes));
-          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-          va[db][j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
-        }
-    };
-    auto qk = [&](int sb, const u32x4 (&ka)[S::kKC]) {
+    constexpr int N_MFMA = decltype(n_mfma_tag)::value;
+    if constexpr (MASK) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[nb][sb][r] = 0.f;
-#pragma unroll
-      for (int kc = 0; kc < S::kKC; ++kc)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) s[nb][sb] = mfma32(ka[kc], qop[nb][kc], s[nb][sb]);
-    };
-    // P = exp2(c s - m) for half sb of row block nb, packed as two P^T B
-    // operands; returns this lane's share of the half's row sum.
-    auto exp_half = [&](int sb, int nb) {
-      // (with an attention mask a row may still have no visible key: its
-      // reference stays -inf and every probability is exp2(-inf) = 0)
-      const float neg_m = (MK != 0 && m_run[nb] == kNegInf) ? 0.f : -m_run[nb];
-      float rs[4] = {0.f, 0.f, 0.f, 0.f};  // short dependency chains
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        float e[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          e[i] = fast_exp2(__builtin_fmaf(s[nb][sb][8 * half + i], c, neg_m));
-          rs[i & 3] += e[i];
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool vis = key < p.Lk && (!CAUSAL || key <= qrow[nb]);
+          s[nb][sb][r] = vis ? s[nb][sb][r] : kNegInf;
         }
-        u32x4 pk;
-        pk[0] = pack_bf16x2(e[0], e[1]);
-        pk[1] = pack_bf16x2(e[2], e[3]);
-        pk[2] = pack_bf16x2(e[4], e[5]);
-        pk[3] = pack_bf16x2(e[6], e[7]);
-        pop[nb][2 * sb + half] = pk;
-      }
-      return (rs[0] + rs[1]) + (rs[2] + rs[3]);
-    };
-    // Softmax of half sb.  N_MFMA products issued just before it are spread
-    // between its vector instructions.
-    auto softmax_half = [&](int sb, auto n_mfma_tag) {
-      constexpr int N_MFMA = decltype(n_mfma_tag)::value;
-      if constexpr (MASK) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3);
-            const bool vis = key < p.Lk && (!CAUSAL || key <= qrow[nb]);
-            s[nb][sb][r] = vis ? s[nb][sb][r] : kNegInf;
-          }
-      }
-      if constexpr (MK != 0) {
-        // Keys 32 sb + 8 j + 4 g + 0..3 of this lane's query row in the mask
-        // tile: a boolean removes pairs, an additive mask enters the raw score
-        // as mask / |scale| (so the exponent gets scale s + mask, in log2 units).
-        const lds_char* mt = lds_b + S::kLdsBytes + buf * MS::kTileBytes;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const lds_char* mrow = mt + (wave * S::kRowsPerWave + 32 * nb + lq) * MS::kRowBytes;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int off = (32 * sb + 8 * j + 4 * g) * MS::kEs;
-            if constexpr (MK == 1) {
-              const uint32_t w = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(mrow + off);
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                s[nb][sb][4 * j + e] = ((w >> (8 * e)) & 0xffu) ? s[nb][sb][4 * j + e] : kNegInf;
-            } else {
-              const u32x2 w = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(mrow + off);
-              s[nb][sb][4 * j + 0] = __builtin_fmaf(bf16_lo(w[0]), p.inv_abs_scale, s[nb][sb][4 * j + 0]);
-              s[nb][sb][4 * j + 1] = __builtin_fmaf(bf16_hi(w[0]), p.inv_abs_scale, s[nb][sb][4 * j + 1]);
-              s[nb][sb][4 * j + 2] = __builtin_fmaf(bf16_lo(w[1]), p.inv_abs_scale, s[nb][sb][4 * j + 2]);
-              s[nb][sb][4 * j + 3] = __builtin_fmaf(bf16_hi(w[1]), p.inv_abs_scale, s[nb][sb][4 * j + 3]);
-            }
-          }
-        }
-      }
-      float ls[NB];
-      bool redo = false;
+    }
+    if constexpr (MK != 0) {
+      // Keys 32 sb + 8 j + 4 g + 0..3 of this lane's query row in the mask
+      // tile: a boolean removes pairs, an additive mask enters the raw score
+      // as mask / |scale| (so the exponent gets scale s + mask, in log2 units).
+      const lds_char* mt = lds_b + MS::kKVBytes + buf * MS::kTileBytes;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        ls[nb] = exp_half(sb, nb);
-        // a row still without a visible key always takes the exact path
-        redo = redo || !(ls[nb] <= kSumGuard) || (MK != 0 && m_run[nb] == kNegInf);
-      }
-      // about 60 vector instructions per row block: one product per share
+        const lds_char* mrow = mt + (wave * S::kRowsPerWave + 32 * nb + lq) * MS::kRowBytes;
 #pragma unroll
-      for (int i = 0; i < N_MFMA; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 56 * NB / N_MFMA, 0);
-      }
-      if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+        for (int j = 0; j < 4; ++j) {
+          const int off = (32 * sb + 8 * j + 4 * g) * MS::kEs;
+          if constexpr (MK == 1) {
+            const uint32_t w = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(mrow + off);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          float mx = kNegInf;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][sb][r]);
-          const float m_new = fmaxf(m_run[nb], max_xor32(mx) * c);  // the scale is positive
-          const float alpha = m_new == m_run[nb] ? 1.f : fast_exp2(m_run[nb] - m_new);
-          m_run[nb] = m_new;
-          l_run[nb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < S::kND; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[nb][db][r] *= alpha;
-          ls[nb] = exp_half(sb, nb);
+            for (int e = 0; e < 4; ++e)
+              s[nb][sb][4 * j + e] = ((w >> (8 * e)) & 0xffu) ? s[nb][sb][4 * j + e] : kNegInf;
+          } else {
+            const u32x2 w = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(mrow + off);
+            s[nb][sb][4 * j + 0] = __builtin_fmaf(bf16_lo(w[0]), p.inv_abs_scale, s[nb][sb][4 * j + 0]);
+            s[nb][sb][4 * j + 1] = __builtin_fmaf(bf16_hi(w[0]), p.inv_abs_scale, s[nb][sb][4 * j + 1]);
+            s[nb][sb][4 * j + 2] = __builtin_fmaf(bf16_lo(w[1]), p.inv_abs_scale, s[nb][sb][4 * j + 2]);
+            s[nb][sb][4 * j + 3] = __builtin_fmaf(bf16_hi(w[1]), p.inv_abs_scale, s[nb][sb][4 * j + 3]);
+          }
         }
       }
+    }
+    float ls[NB];
+    bool redo = false;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) l_run[nb] += ls[nb];
-    };
-
-    constexpr int kQKMfma = S::kKC * NB, kPVMfma = S::kND * 2 * NB;
-    u32x4 ka1[S::kKC], va0[S::kND][2];
-    read_k(buf, 1, ka1);
-    __builtin_amdgcn_s_setprio(2);
-    qk(0, ka_next);
-    __builtin_amdgcn_s_setprio(0);
-    read_v(0, va0);
-    qk(1, ka1);
-    softmax_half(0, std::integral_constant<int, kQKMfma>{});
-    read_v(1, va_last);
-    pv(0, va0);
-    softmax_half(1, std::integral_constant<int, kPVMfma>{});
+    for (int nb = 0; nb < NB; ++nb) {
+      ls[nb] = exp_half(sb, nb);
+      // a row still without a visible key always takes the exact path
+      redo = redo || !(ls[nb] <= kSumGuard) || (MK != 0 && m_run[nb] == kNegInf);
+    }
+    // about 60 vector instructions per row block: one product per share
+#pragma unroll
+    for (int i = 0; i < N_MFMA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 56 * NB / N_MFMA, 0);
+    }
+    if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][sb][r]);
+        const float m_new = fmaxf(m_run[nb], max_xor32(mx) * c);  // the scale is positive
+        const float alpha = m_new == m_run[nb] ? 1.f : fast_exp2(m_run[nb] - m_new);
+        m_run[nb] = m_new;
+        l_run[nb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < S::kND; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[nb][db][r] *= alpha;
+        ls[nb] = exp_half(sb, nb);
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) l_run[nb] += ls[nb];
   };
+
+  constexpr int kQKMfma = S::kKC * NB, kPVMfma = S::kND * 2 * NB;
+  using QKTag = std::integral_constant<int, kQKMfma>;
+  using PVTag = std::integral_constant<int, kPVMfma>;
+  using BothTag = std::integral_constant<int, kQKMfma + kPVMfma>;
 
   // Q must have landed before the first copy: the copies are invisible to the
   // compiler, and a later wait for Q would not know to let them run on.
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-  if (n_tiles > 0) issue_tile(0);
+  if (n_tiles > 0) issue_tile(0, 0);
   if (n_tiles > 1) {
-    issue_tile(1);
+    issue_tile(1, 1);
     __builtin_amdgcn_s_waitcnt(0x0f70 | (S::kCopiesPerWave + MS::kCopiesPerWave));  // vmcnt: tile 0's copies done
   } else {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   }
   __syncthreads();
-  auto active = [&](int t) { return !CAUSAL || t * S::kBC <= wave_last_row; };
-  if (n_tiles > 0 && active(0)) read_k(0, 0, ka_next);
+  auto active = [&](int t) { return t < n_tiles && (!CAUSAL || t * S::kBC <= wave_last_row); };
+  if (active(0)) read_k(0, 0, ka_next);
 
-  // Step t: the front of tile t; then wait for this wave's copies of tile
-  // t + 1 and barrier (all copies of t + 1 are in LDS, every wave has read
-  // all it needs of tile t), copy tile t + 2 into tile t's buffer, read the
-  // first K operands of tile t + 1, and issue tile t's last products.  Tiles
-  // that need no mask for any wave of the workgroup come first; the tail of
-  // the key range and the diagonal tiles follow with the masked path.
-  auto step = [&](auto mask_tag, int t) {
-    const bool act = active(t);
-    if (act) tile_front(mask_tag, t & 1, t * S::kBC);
+  // Between the halves of tile t: wait for this wave's copies of tile t + 1
+  // and barrier (all copies of t + 1 are in LDS, and every wave is done with
+  // the buffer that tile t + 2 refills: tile t's with two buffers, tile
+  // t - 1's with three), copy tile t + 2 into buffer buf2 and read the first
+  // K operands of tile t + 1 from buffer buf1.
+  auto turn = [&](int t, int buf1, int buf2) __attribute__((always_inline)) {
     if (t + 1 < n_tiles) {
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
       __syncthreads();
-      if (t + 2 < n_tiles) issue_tile(t + 2);
-      if (active(t + 1)) read_k((t + 1) & 1, 0, ka_next);
+      if (t + 2 < n_tiles) issue_tile(t + 2, buf2);
+      if (active(t + 1)) read_k(buf1, 0, ka_next);
     }
-    if (act) tile_back();
   };
+  // Tiles that need no mask for any wave of the workgroup come first; the
+  // tail of the key range and the diagonal tiles follow with the masked
+  // path.
   int n_plain = min(n_tiles, n_full);
   if (CAUSAL) n_plain = min(n_plain, (q0 + 1) / S::kBC);
-  int t = 0;
-  for (; t < n_plain; ++t) step(std::false_type{}, t);
-  for (; t < n_tiles; ++t) step(std::true_type{}, t);
+  if constexpr (kPipe) {
+    // Before tile 0 there is no earlier half: its products run on zero
+    // probabilities and zero operands and add nothing, which keeps one copy
+    // of the step (a separate first step costs registers).
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 2; i < 4; ++i) pop[nb][i] = zero16();
+#pragma unroll
+    for (int db = 0; db < S::kND; ++db)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) va_last[db][j] = zero16();
+    if (active(0)) qk(0, ka_next);
+    // Phase A of tile t (the wave is active there).  The V^T operands of the
+    // first half are read at its end, before the barrier; those of the
+    // second half at the end of phase B (the buffer of tile t is refilled
+    // only at the barrier of tile t + 1).
+    auto phase_a = [&](auto mask_tag, int t, int buf) __attribute__((always_inline)) {
+      read_k(buf, 1, ka1);
+      pv(1, va_last);
+      qk(1, ka1);
+      softmax_half(mask_tag, buf, t * S::kBC, 0, BothTag{});
+      read_v(buf, 0, va0);
+    };
+    // Phase B; the products S(t + 1, 0) are issued whether or not the wave
+    // is active in tile t + 1 (then on stale operands, and never used), so
+    // that they stay in one scheduling region with the softmax.
+    auto phase_b = [&](auto mask_tag, int t, int buf) __attribute__((always_inline)) {
+      pv(0, va0);
+      qk(0, ka_next);
+      softmax_half(mask_tag, buf, t * S::kBC, 1, BothTag{});
+      read_v(buf, 1, va_last);
+      if (!active(t + 1)) pv(1, va_last);  // the wave's last tile
+    };
+    // Tile t lives in buffer t % 3.  BUF is that buffer when the caller
+    // knows it at compile time (then every LDS address of the step is a
+    // register plus a constant offset), -1 otherwise.
+    auto step = [&](auto mask_tag, int t, auto buf_tag) __attribute__((always_inline)) {
+      constexpr int BUF = decltype(buf_tag)::value;
+      const int buf = BUF >= 0 ? BUF : (int)((unsigned)t % 3);
+      const int buf1 = BUF >= 0 ? (BUF + 1) % 3 : (int)((unsigned)(t + 1) % 3);
+      const int buf2 = BUF >= 0 ? (BUF + 2) % 3 : (int)((unsigned)(t + 2) % 3);
+      const bool act = active(t);
+      if (act) phase_a(mask_tag, t, buf);
+      turn(t, buf1, buf2);
+      if (act) phase_b(mask_tag, t, buf);
+    };
+    // Unmasked tiles three at a time (one pass through the three buffers);
+    // the last one or two of them run with the masked path, which is exact
+    // for them as well.
+    int t = 0;
+    for (; t + 3 <= n_plain; t += 3) {
+      step(std::false_type{}, t, std::integral_constant<int, 0>{});
+      step(std::false_type{}, t + 1, std::integral_constant<int, 1>{});
+      step(std::false_type{}, t + 2, std::integral_constant<int, 2>{});
+    }
+    for (; t < n_tiles; ++t) step(std::true_type{}, t, std::integral_constant<int, -1>{});
+  } else {
+    auto step = [&](auto mask_tag, int t) __attribute__((always_inline)) {
+      const bool act = active(t);
+      const int buf = t & 1, kv0 = t * S::kBC;
+      if (act) {
+        read_k(buf, 1, ka1);
+        __builtin_amdgcn_s_setprio(2);
+        qk(0, ka_next);
+        __builtin_amdgcn_s_setprio(0);
+        read_v(buf, 0, va0);
+        qk(1, ka1);
+        softmax_half(mask_tag, buf, kv0, 0, QKTag{});
+        read_v(buf, 1, va_last);
+        pv(0, va0);
+        softmax_half(mask_tag, buf, kv0, 1, PVTag{});
+      }
+      turn(t, (t + 1) & 1, t & 1);
+      if (act) {
+        __builtin_amdgcn_s_setprio(2);
+        pv(1, va_last);
+        __builtin_amdgcn_s_setprio(0);
+      }
+    };
+    int t = 0;
+    for (; t < n_plain; ++t) step(std::false_type{}, t);
+    for (; t < n_tiles; ++t) step(std::true_type{}, t);
+  }
 
   // ---- epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2 ----
 #pragma unroll
