@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256, 3) void attn_decode_split_kernel(DecodeParams 
   const int b = unit / (p.n_hgroups * p.Hkv);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;   // query column / A-operand row
   const int g = lane >> 4;   // 16-lane row
 
@@ -136,16 +136,17 @@ __global__ __launch_bounds__(256, 3) void attn_decode_split_kernel(DecodeParams 
   u32x4 kreg[2][KC];
   u32x4 vreg[8];
   if (w0 < w1) {
-    // Q must have landed first so that waits for it do not also wait for
-    // the cache rows issued below.
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     load_k(w0, kreg);
     load_v(w0, vreg);
   }
 
   // Each step's loads for the next 32 keys are issued as soon as the
   // registers they land in have been consumed, so cache rows stay in flight
-  // while this step computes.
+  // while this step computes.  They are issued on the last step too (its rows
+  // clamp to the last slot, in bounds and already cached): loads issued on
+  // every path keep the load counter's order known, so each wait covers
+  // exactly the loads it needs (conditional prefetches made the compiler
+  // also wait for the next step's K rows before this step's P V).
   for (int base = w0; base < w1; base += 32) {
     const int nxt = base + 32;
 
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(256, 3) void attn_decode_split_kernel(DecodeParams 
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) s[kb] = mfma16(kreg[kb][kc], qop[kc], s[kb]);
     }
-    if (nxt < w1) load_k(nxt, kreg);
+    load_k(nxt, kreg);
 
     float mx = kNegInf;
 #pragma unroll
@@ -209,7 +210,7 @@ __global__ __launch_bounds__(256, 3) void attn_decode_split_kernel(DecodeParams 
                                      (t & 1) ? 0x07060302u : 0x05040100u);
       oacc[t] = mfma16(a, pop, oacc[t]);
     }
-    if (nxt < w1) load_v(nxt, vreg);
+    load_v(nxt, vreg);
   }
 
   // Combine the 4 waves' partial results in LDS.

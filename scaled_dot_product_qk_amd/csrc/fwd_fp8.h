@@ -49,6 +49,15 @@ __device__ __forceinline__ f32x16 mfma32_fp8(const u32x8& a, const u32x8& b, con
                                                          c, 0, 0, 0, 127, 0, 127);
 }
 
+// 16x16x128 e4m3 product with fp32 accumulation (unit block scales).  Lane l
+// holds A row l % 16 and B column l % 16, each with the 32 k values of
+// k-group l / 16 (the same lane/byte -> k assignment for A and B); C row
+// 4 (l / 16) + i, column l % 16 in register i.
+__device__ __forceinline__ f32x4 mfma16_fp8(const u32x8& a, const u32x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(__builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, b),
+                                                          c, 0, 0, 0, 127, 0, 127);
+}
+
 // Four fp32 values to e4m3 codes (nearest even) packed low byte first.
 __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
@@ -214,7 +223,22 @@ attn_fwd_fp8_kernel(FwdParams p) {
   for (int i = 0; i < S::kND; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = kNegInf, l_run = 0.f;  // l_run: the whole row's sum, in both lanes of the query
+
+  // Row sums of P~ on the matrix core.  Read as the B operand of a 16x16x128
+  // product, the P^T operand of lane l sits in column l % 16, k-group
+  // j = l / 16, and holds 32 keys of query l % 32: k-groups 0 and 2 hold the
+  // 64 keys of queries 0-15, k-groups 1 and 3 those of queries 16-31.  An A
+  // operand whose row m is e4m3 1.0 on the k-groups j with j % 2 ==
+  // (m / 4) % 2 (zero on the others) makes C row m, column n the sum over
+  // the half's 64 keys of query n + 16 ((m / 4) % 2); register 0 of lane l
+  // (row 4 (l / 16), column l % 16) is then the sum for query l % 32.
+  u32x8 sum_sel;
+  {
+    const uint32_t w = ((lane >> 2) & 1) == ((lane >> 4) & 1) ? 0x38383838u : 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sum_sel[i] = w;
+  }
 
   u32x8 ka_next[2][S::kKC];  // K operands of the next tile's first half (two 32-key blocks)
   u32x8 va_last[S::kND];     // V^T operands of this tile's second half
@@ -272,10 +296,11 @@ attn_fwd_fp8_kernel(FwdParams p) {
       }
     };
     // P~ = e4m3(exp2(c s - m)) for half sb, packed as the P^T operand;
-    // returns this lane's share of the half's sum of P~.
+    // returns the half's row sum of P~ for this lane's query, formed on the
+    // matrix core from the same rounded values that weight V (fp32
+    // accumulation), without unpacking them on the vector ALU: see sum_sel.
     auto exp_half = [&](int sb) {
       const float neg_m = -m_run;
-      float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -283,16 +308,10 @@ attn_fwd_fp8_kernel(FwdParams p) {
           float e[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) e[i] = fast_exp2(__builtin_fmaf(s[sb][j][4 * q + i], c, neg_m));
-          const uint32_t w = pack_e4m3x4(e[0], e[1], e[2], e[3]);
-          pop[sb][4 * j + q] = w;
-          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-          rs[0] += lo[0];
-          rs[1] += lo[1];
-          rs[2] += hi[0];
-          rs[3] += hi[1];
+          pop[sb][4 * j + q] = pack_e4m3x4(e[0], e[1], e[2], e[3]);
         }
-      return (rs[0] + rs[1]) + (rs[2] + rs[3]);
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      return mfma16_fp8(sum_sel, pop[sb], z)[0];
     };
     auto softmax_half = [&](int sb, auto n_mfma_tag) {
       constexpr int N_MFMA = decltype(n_mfma_tag)::value;
@@ -376,7 +395,7 @@ attn_fwd_fp8_kernel(FwdParams p) {
   for (; t < n_tiles; ++t) step(std::true_type{}, t);
 
   // ---- epilogue: O = v_descale O_acc / l, LSE = (m + log2 l) ln 2 ----
-  const float l_tot = sum_xor32(l_run);
+  const float l_tot = l_run;
   if (qrow < p.Lq) {
     const float mul = l_tot > 0.f ? p.o_mul / l_tot : 0.f;
     uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)qrow * p.o_st;
