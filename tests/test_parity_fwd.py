@@ -211,3 +211,39 @@ def test_workload_fwd_causal_gqa_n8192_sampled_rows(dev):
     check(np.concatenate(os_), np.concatenate(osr), np.concatenate(ls), np.concatenate(lsr),
           "bf16", w.name)
     assert np.isfinite(o_np).all() and np.isfinite(lse_np).all()
+
+
+# Head_dim 64 without causal masking or a mask runs a schedule that pipelines
+# the two key halves across tiles, rotates through three LDS buffers, and
+# hands the last one or two unmasked tiles to the masked loop.  These key
+# counts give 1 to 7 key tiles, full and ragged, so every position of the
+# three-buffer rotation is both the last tile and the masked tail.
+PIPE_LK = [1, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 257, 320, 383, 384, 385, 448]
+
+
+@pytest.mark.parametrize("lk", PIPE_LK)
+def test_bf16_d64_pipeline_tiles(dev, lk):
+    w = wl.FwdWorkload("pipe", 1, 3, 1, 150, lk, 64, "bf16", False, 7000 + lk)
+    full_check(w, dev, label=f"bf16 d64 pipelined Lk={lk}")
+
+
+@pytest.mark.parametrize("lk", [64, 192, 448])
+def test_bf16_d64_pipeline_rescale(dev, lk):
+    """Scores three times larger: the reference max moves (and O is rescaled)
+    in later tiles, between pipelined halves."""
+    w = wl.FwdWorkload("pipe_big", 1, 2, 2, 200, lk, 64, "bf16", False, 7100 + lk)
+    full_check(w, dev, q_mul=3.0, label=f"bf16 d64 pipelined q x3 Lk={lk}")
+
+
+def test_bf16_d64_pipeline_rising_scores(dev):
+    """Keys whose scores grow along the sequence: the reference max moves up
+    in almost every tile, so O is rescaled while the previous half's products
+    are still in flight in the pipelined schedule."""
+    w = wl.FwdWorkload("pipe_rise", 1, 2, 1, 130, 448, 64, "bf16", False, 7200)
+    q, k, v = wl.make_fwd_inputs(w)
+    ramp = torch.linspace(0.5, 4.0, w.Lk).view(1, 1, w.Lk, 1)
+    k = (k.float() * ramp).to(torch.bfloat16)
+    q = (q.float().abs() * torch.sign(k.float().mean(dim=2, keepdim=True))).to(torch.bfloat16)
+    o, lse = run_gpu(q, k, v, dev, causal=False)
+    o_ref, lse_ref = orc.attention_forward(q, k, v, causal=False)
+    check(to_np(o), o_ref, to_np(lse), lse_ref, "bf16", "bf16 d64 pipelined rising scores")
