@@ -259,19 +259,24 @@ attn_status_t attn_fwd_varlen(const attn_fwd_varlen_args_t *args, void *stream);
 
 /*
  * attn_decode_workspace_bytes - bytes of device workspace attn_decode needs
- * for these sizes (fp32 partial outputs and log-sum-exps of every key chunk).
- * Returns 0 for invalid sizes.
+ * for these sizes: fp32 partial outputs and log-sum-exps, for every query
+ * head of every sequence, of the (Lmax - 1) / 512 + 2 pieces of the split
+ * that one sequence's cache slots can span at most.  Returns 0 for invalid
+ * sizes.
  */
 size_t attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Lmax, int64_t d);
 
 /*
- * attn_decode - split-KV decode: one kernel computes a partial (O, LSE) per
- * (sequence, kv head, key chunk), a second merges the chunks of each query
- * head.  `workspace` is caller-owned device memory of at least
+ * attn_decode - split-KV decode: one kernel lays the cache slots of every
+ * (sequence, kv head) end to end, cuts them into equal pieces (one per
+ * workgroup, at least 512 slots each) and computes a partial (O, LSE) per
+ * query head for each (sequence, kv head) a piece touches; a second kernel
+ * merges the partials of each query head.  `workspace` is caller-owned device memory of at least
  * attn_decode_workspace_bytes(B, Hq, Lmax, d) bytes, 256-byte aligned; its
  * contents on entry do not matter and are overwritten.  Calls that share a
  * workspace must be ordered on one stream.
- * Supported: dtype bf16; d in {64, 128}; Hq % Hkv == 0.  The query heads of
+ * Supported: dtype bf16; d in {64, 128}; Hq % Hkv == 0; B * Lmax < 2^31
+ * (ATTN_ERR_UNSUPPORTED otherwise).  The query heads of
  * one kv head are served 16 at a time, so a group larger than 16 reads its
  * keys and values once per 16 query heads.  B == 0 or Hq == 0 is a no-op;
  * Lmax == 0 writes O = 0 and LSE = -inf.  Exactly two kernels are enqueued

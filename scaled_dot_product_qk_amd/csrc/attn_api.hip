@@ -42,7 +42,24 @@ float effective_scale(float scale, int64_t d) {
   return scale == 0.f ? 1.0f / std::sqrt((float)d) : scale;
 }
 
-int64_t decode_chunks(int64_t Lmax) { return (Lmax + kDecChunk - 1) / kDecChunk; }
+// Workspace rows per (sequence, query head): the most pieces of the balanced
+// decode split one sequence's slots can span (pieces hold at least
+// kDecMinPiece slots, so L slots touch at most (L - 1) / kDecMinPiece + 2).
+int64_t decode_pieces(int64_t Lmax) { return Lmax > 0 ? (Lmax - 1) / kDecMinPiece + 2 : 0; }
+
+// Compute units of the current device (queried once per device).
+int device_cu_count() {
+  static int counts[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev >= 64) dev = 63;
+  if (counts[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    counts[dev] = n;
+  }
+  return counts[dev];
+}
 
 }  // namespace
 
@@ -513,7 +530,7 @@ extern "C" attn_status_t attn_bwd(const attn_bwd_args_t* a, void* workspace, siz
 
 extern "C" size_t attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Lmax, int64_t d) {
   if (B < 0 || Hq < 0 || Lmax < 0 || d <= 0) return 0;
-  const int64_t rows = B * Hq * decode_chunks(Lmax);
+  const int64_t rows = B * Hq * decode_pieces(Lmax);
   const int64_t obytes = (rows * d * 4 + 255) / 256 * 256;
   return (size_t)(obytes + rows * 4);
 }
@@ -536,7 +553,8 @@ extern "C" attn_status_t attn_validate_decode(const attn_decode_args_t* a) {
       !strides_ok(a->k_strides, 3, 2) || !strides_ok(a->v_strides, 3, 2))
     return ATTN_ERR_LAYOUT;
   const int64_t hgroups = (a->Hq / a->Hkv + kDecHeadsPerGroup - 1) / kDecHeadsPerGroup;
-  if (a->Lmax > kI32Max || decode_chunks(a->Lmax) > kGridYMax || a->B * a->Hq > kI32Max ||
+  // the lengths' total must fit 32 bits
+  if (a->Lmax > kI32Max || a->B * a->Lmax > kI32Max || a->B * a->Hq > kI32Max ||
       a->B * a->Hkv * hgroups > kI32Max)
     return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
@@ -544,9 +562,8 @@ extern "C" attn_status_t attn_validate_decode(const attn_decode_args_t* a) {
 
 template <int D>
 static attn_status_t launch_decode(const DecodeParams& p, int B, hipStream_t s) {
-  if (p.n_chunks > 0) {
-    hipLaunchKernelGGL(attn_decode_split_kernel<D>, dim3(B * p.Hkv * p.n_hgroups, p.n_chunks),
-                       dim3(256), 0, s, p);
+  if (p.Lmax > 0) {
+    hipLaunchKernelGGL(attn_decode_split_kernel<D>, dim3(p.n_wg), dim3(256), 0, s, p);
     if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
   }
   hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3(B * p.Hq), dim3(D), 0, s, p);
@@ -565,7 +582,7 @@ extern "C" attn_status_t attn_decode(const attn_decode_args_t* a, void* workspac
 
   DecodeParams p;
   p.q = a->q; p.k = a->k_cache; p.v = a->v_cache; p.seqlens = a->seqlens;
-  const int64_t rows = a->B * a->Hq * decode_chunks(a->Lmax);
+  const int64_t rows = a->B * a->Hq * decode_pieces(a->Lmax);
   p.o_part = reinterpret_cast<float*>(workspace);
   p.lse_part = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
                                         (rows * a->d * 4 + 255) / 256 * 256);
@@ -578,8 +595,16 @@ extern "C" attn_status_t attn_decode(const attn_decode_args_t* a, void* workspac
   p.Hkv = (int)a->Hkv;
   p.group = (int)(a->Hq / a->Hkv);
   p.Lmax = (int)a->Lmax;
-  p.n_chunks = (int)decode_chunks(a->Lmax);
+  p.B = (int)a->B;
   p.n_hgroups = (p.group + kDecHeadsPerGroup - 1) / kDecHeadsPerGroup;
+  p.n_pieces = (int)decode_pieces(a->Lmax);
+  // One piece per resident split workgroup, fewer when even the largest
+  // possible total (every sequence at Lmax) would leave pieces below the minimum.
+  {
+    const int64_t most = (a->Hkv * p.n_hgroups * a->B * a->Lmax + kDecMinPiece - 1) / kDecMinPiece;
+    const int64_t want = (int64_t)device_cu_count() * kDecGroupsPerCU;
+    p.n_wg = (int)(most < want ? (most > 0 ? most : 1) : want);
+  }
   p.scale_log2 = effective_scale(a->scale, a->d) * kLog2e;
   switch (a->d) {
     case 64: return launch_decode<64>(p, (int)a->B, s);

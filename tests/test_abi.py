@@ -160,7 +160,7 @@ def test_decode_valid(d, Hq, Hkv):
     (dict(Hkv=3), SHAPE), (dict(Hkv=0), SHAPE), (dict(Lmax=-1), SHAPE),
     (dict(scale=float("nan")), SHAPE),
     (dict(q=P + 2), LAYOUT), (dict(seqlens=P + 2), LAYOUT), (dict(ks=(8 * 1000 * 128, 1000 * 128, 130)), LAYOUT),
-    (dict(Lmax=40_000_000), UNSUP), (dict(Lmax=2 ** 31), UNSUP),
+    (dict(B=64, Lmax=40_000_000), UNSUP), (dict(Lmax=2 ** 31), UNSUP),
 ])
 def test_decode_rejections(kw, status):
     assert vdec(**kw) == status
@@ -171,13 +171,14 @@ def test_decode_rejections(kw, status):
 def test_decode_workspace_rules():
     L = sdpa.lib()
     need = sdpa.attn_decode_workspace_bytes(4, 8, 1000, 128)
-    # 2 chunks of 512 slots: O partials 4*8*2*128 floats (256-aligned) + LSE partials
-    assert need == 4 * 8 * 2 * 128 * 4 + 4 * 8 * 2 * 4
+    # 1000 slots span at most 3 pieces of >= 512 slots: O partials 4*8*3*128 floats
+    # (256-aligned) + LSE partials
+    assert need == 4 * 8 * 3 * 128 * 4 + 4 * 8 * 3 * 4
     assert L.attn_decode(ctypes.byref(dec_args()), None, need, None) == WS
     assert L.attn_decode(ctypes.byref(dec_args()), P, need - 1, None) == WS
     assert L.attn_decode(ctypes.byref(dec_args()), P + 16, need, None) == LAYOUT
     assert sdpa.attn_decode_workspace_bytes(-1, 8, 10, 128) == 0
-    assert sdpa.attn_decode_workspace_bytes(64, 32, 8192, 128) == 64 * 32 * 16 * 129 * 4
+    assert sdpa.attn_decode_workspace_bytes(64, 32, 8192, 128) == 64 * 32 * 17 * 129 * 4
     assert sdpa.attn_decode_workspace_bytes(2, 2, 0, 128) == 0
 
 
