@@ -736,29 +736,54 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
   }
 
   // ---- epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2 ----
+  // O is written once and not read again by this call, so it bypasses the
+  // caches' allocation (non-temporal stores): left dirty in the caches it
+  // would be written back later, taking HBM bandwidth from whatever runs
+  // next (a decode step, say).  Non-temporal stores must cover whole lines to
+  // stay cheap, so at head_dim 64 and 128 each wave first turns its rows
+  // around in LDS (16-byte chunks XOR-swizzled by row) and then stores whole
+  // rows, 16 bytes per lane.
+  constexpr bool kStaged = D == 64 || D == 128;
+  constexpr int kCPR = D / 8;  // 16-byte chunks per row
+  constexpr int kRowB = 2 * D;
+  lds_char* const st = lds_b + wave * S::kRowsPerWave * kRowB;
+  if constexpr (kStaged) __syncthreads();  // every wave is done with the key/value buffers
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const float l_tot = sum_xor32(l_run[nb]);
-    if (qrow[nb] < p.Lq) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + b * p.o_sb + h * p.o_sh +
-                       (int64_t)qrow[nb] * p.o_st;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (g == 0 && qrow[nb] < p.Lq) {
+      const float lse = l_tot > 0.f ? (m_run[nb] + log2f(l_tot)) * kLn2 : kNegInf;
+      __builtin_nontemporal_store(lse, &p.lse[b * p.lse_sb + h * p.lse_sh + qrow[nb]]);
+    }
+    uint16_t* const orow = reinterpret_cast<uint16_t*>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)qrow[nb] * p.o_st;
+    const int r = 32 * nb + lq;
 #pragma unroll
-      for (int db = 0; db < S::kND; ++db)
+    for (int db = 0; db < S::kND; ++db)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = 32 * db + 8 * j + 4 * g;
-          if (d < D) {
-            u32x2 w;
-            w[0] = pack_bf16x2(oacc[nb][db][4 * j + 0] * inv, oacc[nb][db][4 * j + 1] * inv);
-            w[1] = pack_bf16x2(oacc[nb][db][4 * j + 2] * inv, oacc[nb][db][4 * j + 3] * inv);
-            *reinterpret_cast<u32x2*>(orow + d) = w;
-          }
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * db + 8 * j + 4 * g;
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[nb][db][4 * j + 0] * inv, oacc[nb][db][4 * j + 1] * inv);
+        w[1] = pack_bf16x2(oacc[nb][db][4 * j + 2] * inv, oacc[nb][db][4 * j + 3] * inv);
+        if constexpr (kStaged) {
+          *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+              st + r * kRowB + 16 * ((d >> 3) ^ (r & (kCPR - 1))) + 8 * g) = w;
+        } else if (d < D && qrow[nb] < p.Lq) {
+          __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(orow + d));
         }
-      if (g == 0) {
-        const float lse = l_tot > 0.f ? (m_run[nb] + log2f(l_tot)) * kLn2 : kNegInf;
-        p.lse[b * p.lse_sb + h * p.lse_sh + qrow[nb]] = lse;
       }
+  }
+  if constexpr (kStaged) {
+    uint16_t* const obase = reinterpret_cast<uint16_t*>(p.o) + b * p.o_sb + h * p.o_sh;
+#pragma unroll
+    for (int i = 0; i < S::kRowsPerWave * kCPR / 64; ++i) {
+      const int idx = 64 * i + lane;
+      const int r = idx / kCPR, c = idx % kCPR;
+      const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+          st + r * kRowB + 16 * (c ^ (r & (kCPR - 1))));
+      const int row = row0 + r;
+      if (row < p.Lq) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(obase + (int64_t)row * p.o_st + 8 * c));
     }
   }
 }
