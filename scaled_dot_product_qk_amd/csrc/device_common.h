@@ -87,11 +87,17 @@ __device__ __forceinline__ float sum_xor16(float x) {
 // the compiler neither counts the copies among its outstanding loads nor makes
 // LDS reads and barriers wait for them: kernels wait for their own copies
 // (vmcnt) before the barrier that publishes them.
+// Being inline assembly, the copies are also invisible to the compiler's
+// hazard checks.  A vector instruction that writes an SGPR (v_readlane when an
+// SGPR spill is reloaded, v_readfirstlane) needs 5 wait states before a vector
+// memory instruction may read that SGPR as its address, and the compiler may
+// place such a write right before a copy, which would then read a stale base.
+// So every copy starts with its own s_nop 4.
 __device__ __forceinline__ void lds_copy16(const void* base, uint32_t off, uint32_t lds_base) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_base) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_base) : "memory");
 }
 __device__ __forceinline__ void lds_copy4(const void* base, uint32_t off, uint32_t lds_base) {
-  asm volatile("global_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_base) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_base) : "memory");
 }
 
 __device__ __forceinline__ u32x4 load16(const void* p) {
