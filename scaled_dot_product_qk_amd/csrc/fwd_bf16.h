@@ -531,9 +531,37 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
       pk[1] = pack_bf16x2(e[2], e[3]);
       pk[2] = pack_bf16x2(e[4], e[5]);
       pk[3] = pack_bf16x2(e[6], e[7]);
+      // keep the packs here, among the products: the compiler would
+      // otherwise sink them past the guard's branch (the exact path forms
+      // them again), where they run with no product beside them
+      asm volatile("" : "+v"(pk[0]), "+v"(pk[1]), "+v"(pk[2]), "+v"(pk[3]));
       pop[nb][2 * sb + half] = pk;
     }
     return (rs[0] + rs[1]) + (rs[2] + rs[3]);
+  };
+  // The end of a half's softmax: if the sum guard failed for some lane, take
+  // the half's max, move the reference, rescale O and l and form the
+  // probabilities again; then add the half's sums to l.
+  auto finish_half = [&](int sb, bool redo, float (&ls)[NB]) __attribute__((always_inline)) {
+    if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][sb][r]);
+        const float m_new = fmaxf(m_run[nb], max_xor32(mx) * c);  // the scale is positive
+        const float alpha = m_new == m_run[nb] ? 1.f : fast_exp2(m_run[nb] - m_new);
+        m_run[nb] = m_new;
+        l_run[nb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < S::kND; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[nb][db][r] *= alpha;
+        ls[nb] = exp_half(sb, nb);
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) l_run[nb] += ls[nb];
   };
   // Softmax of half sb of the tile in buffer buf starting at key kv0; MASK
   // selects the variant that masks keys beyond Lk and (causal) keys after the
@@ -592,25 +620,62 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 56 * NB / N_MFMA, 0);
     }
-    if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+    finish_half(sb, redo, ls);
+  };
+
+  // Pipelined schedule, tiles without a mask: the 16 products of a phase —
+  // P V of the other half ob = 1 - sb, then the scores of the next half ob —
+  // and the softmax of half sb in a fixed interleave, one product per two
+  // probabilities (two FMAs, two exponentials, two sums, one pack), each
+  // group closed by a scheduling barrier.  Left to the scheduler, the
+  // products of a phase bunched together and the vector work ran alone after
+  // them.  The arithmetic and its order are those of exp_half.
+  auto fused_half = [&](int sb, const u32x4 (&va)[S::kND][2], const u32x4 (&ka)[S::kKC])
+                        __attribute__((always_inline)) {
+    if constexpr (kPipe) {
+      static_assert(NB == 2 && S::kND == 2 && S::kKC == 4, "one product per two probabilities");
+      const int ob = 1 - sb;
+      float rs[NB][4];
+      u32x4 pk[NB][2];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[nb][ob][r] = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (k < 8) {
+          const int db = k >> 2, j = (k >> 1) & 1, nb = k & 1;
+          oacc[nb][db] = mfma32(va[db][j], pop[nb][2 * ob + j], oacc[nb][db]);
+        } else {
+          const int kc = (k - 8) >> 1, nb = k & 1;
+          s[nb][ob] = mfma32(ka[kc], qop[nb][kc], s[nb][ob]);
+        }
+        const int nb = k >> 3, w = k & 7;  // probabilities 2w, 2w + 1 of row block nb
+        const float e0 = fast_exp2(__builtin_fmaf(s[nb][sb][2 * w], c, -m_run[nb]));
+        const float e1 = fast_exp2(__builtin_fmaf(s[nb][sb][2 * w + 1], c, -m_run[nb]));
+        if (w < 2) {
+          rs[nb][(2 * w) & 3] = e0;
+          rs[nb][(2 * w + 1) & 3] = e1;
+        } else {
+          rs[nb][(2 * w) & 3] += e0;
+          rs[nb][(2 * w + 1) & 3] += e1;
+        }
+        uint32_t pw = pack_bf16x2(e0, e1);
+        asm volatile("" : "+v"(pw));
+        pk[nb][w >> 2][w & 3] = pw;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      float ls[NB];
+      bool redo = false;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][sb][r]);
-        const float m_new = fmaxf(m_run[nb], max_xor32(mx) * c);  // the scale is positive
-        const float alpha = m_new == m_run[nb] ? 1.f : fast_exp2(m_run[nb] - m_new);
-        m_run[nb] = m_new;
-        l_run[nb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < S::kND; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[nb][db][r] *= alpha;
-        ls[nb] = exp_half(sb, nb);
+        ls[nb] = (rs[nb][0] + rs[nb][1]) + (rs[nb][2] + rs[nb][3]);
+        pop[nb][2 * sb] = pk[nb][0];
+        pop[nb][2 * sb + 1] = pk[nb][1];
+        redo = redo || !(ls[nb] <= kSumGuard);
       }
+      finish_half(sb, redo, ls);
     }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) l_run[nb] += ls[nb];
   };
 
   constexpr int kQKMfma = S::kKC * NB, kPVMfma = S::kND * 2 * NB;
@@ -669,18 +734,26 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
     // only at the barrier of tile t + 1).
     auto phase_a = [&](auto mask_tag, int t, int buf) __attribute__((always_inline)) {
       read_k(buf, 1, ka1);
-      pv(1, va_last);
-      qk(1, ka1);
-      softmax_half(mask_tag, buf, t * S::kBC, 0, BothTag{});
+      if constexpr (!decltype(mask_tag)::value) {
+        fused_half(0, va_last, ka1);
+      } else {
+        pv(1, va_last);
+        qk(1, ka1);
+        softmax_half(mask_tag, buf, t * S::kBC, 0, BothTag{});
+      }
       read_v(buf, 0, va0);
     };
     // Phase B; the products S(t + 1, 0) are issued whether or not the wave
     // is active in tile t + 1 (then on stale operands, and never used), so
     // that they stay in one scheduling region with the softmax.
     auto phase_b = [&](auto mask_tag, int t, int buf) __attribute__((always_inline)) {
-      pv(0, va0);
-      qk(0, ka_next);
-      softmax_half(mask_tag, buf, t * S::kBC, 1, BothTag{});
+      if constexpr (!decltype(mask_tag)::value) {
+        fused_half(1, va0, ka_next);
+      } else {
+        pv(0, va0);
+        qk(0, ka_next);
+        softmax_half(mask_tag, buf, t * S::kBC, 1, BothTag{});
+      }
       read_v(buf, 1, va_last);
       if (!active(t + 1)) pv(1, va_last);  // the wave's last tile
     };
