@@ -42,6 +42,21 @@ def test_decode_small(dev, d, Hq, Hkv):
     assert (o[0] == 0).all().item() and torch.isneginf(lse[0]).all().item()
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_many_short_sequences(dev, d):
+    """300 sequences of 0..200 slots (every 17th empty): the split kernel's
+    prefix sums over the lengths take five 64-sequence passes, and one piece
+    of the balanced split (at least 512 slots) spans several sequences."""
+    B = 300
+    g = torch.Generator().manual_seed(81 + d)
+    lens = torch.randint(0, 201, (B,), generator=g, dtype=torch.int32)
+    lens[::17] = 0
+    w = wl.DecodeWorkload("dec_many", B, 8, 2, 200, d, 1, 200, "bf16", 80 + d)
+    o, lse, o_ref, lse_ref, _ = run_decode(w, dev, lengths=lens)
+    check(to_np(o), o_ref, to_np(lse), lse_ref, "bf16", f"decode B=300 d{d}")
+    assert (o[0] == 0).all().item() and torch.isneginf(lse[0]).all().item()
+
+
 def test_decode_lengths_beyond_cache_are_clamped(dev):
     w = wl.DecodeWorkload("dec_clamp", 3, 8, 2, 600, 128, 1, 600, "bf16", 77)
     o, lse, o_ref, lse_ref, _ = run_decode(w, dev, lengths=torch.tensor([-5, 600, 100000]),
