@@ -66,7 +66,8 @@ def test_long_sequence_fp8(dev):
 
 
 def test_long_decode(dev):
-    """A 65536-slot cache: 128 key chunks per sequence, lengths at both ends."""
+    """A 65536-slot cache, lengths at both ends: the longest sequence spans
+    several pieces of the balanced split (at least 512 slots each)."""
     w = wl.DecodeWorkload("long_dec", 3, 8, 2, 65536, 128, 1, 65536, "bf16", 8005)
     lens = torch.tensor([65536, 30001, 1], dtype=torch.int32)
     q, kc, vc, lens = wl.make_decode_inputs(w, poison_tail=True, lengths=lens)
