@@ -187,13 +187,15 @@ __global__ __launch_bounds__(256, kDecGroupsPerCU) void attn_decode_split_kernel
     const int w1 = min(w0 + share, k1);
     const int last = w1 - 1;  // slots beyond it are read from it (in bounds) and masked
 
+    // The cache is streamed once: its rows are read with non-temporal loads,
+    // so they do not displace what the caches hold for other work.
     // K rows as the A operand of S^T: lane row n of 16-key block kb.
     auto load_k = [&](int base, u32x4 (&kr)[2][KC]) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const uint16_t* row = kg + (int64_t)min(base + 16 * kb + n, last) * p.k_st;
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) kr[kb][kc] = load16(row + 8 * (4 * kc + g));
+        for (int kc = 0; kc < KC; ++kc) kr[kb][kc] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + 8 * (4 * kc + g)));
       }
     };
     // V rows for the transposed A operand: lane (n, g) loads 8 rows, head_dim
@@ -202,7 +204,7 @@ __global__ __launch_bounds__(256, kDecGroupsPerCU) void attn_decode_split_kernel
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int key = min(base + 16 * (i >> 2) + 4 * g + (i & 3), last);
-        vr[i] = (8 * n < D) ? load16(vg + (int64_t)key * p.v_st + 8 * n) : zero16();
+        vr[i] = (8 * n < D) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vg + (int64_t)key * p.v_st + 8 * n)) : zero16();
       }
     };
 
