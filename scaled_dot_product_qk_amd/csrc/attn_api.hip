@@ -474,7 +474,8 @@ template <int D>
 static attn_status_t launch_bwd(const BwdParams& p, bool causal, hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.Hq * p.Lq;
   if (rows > 0) {
-    hipLaunchKernelGGL(attn_bwd_delta_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attn_bwd_delta_kernel<D>, dim3((unsigned)((rows + kDeltaRowsPerBlock<D> - 1) / kDeltaRowsPerBlock<D>)),
+                       dim3(256), 0, s, p);
     if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
   }
   const int g_kv = p.B * p.Hkv * ((p.Lk + 127) / 128);

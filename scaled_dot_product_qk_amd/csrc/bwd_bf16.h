@@ -9,7 +9,8 @@
 // dQ = scale dS K, dK = scale dS^T Q.
 //
 // Three kernels:
-//   * attn_bwd_delta_kernel: per query row, (LSE log2 e, D) into the workspace;
+//   * attn_bwd_delta_kernel: per query row, (LSE log2 e, D) into the workspace
+//     (each row read by a group of adjacent lanes, whole rows per load);
 //   * attn_bwd_dkdv_kernel: one workgroup per (batch, kv head, 128 keys); each
 //     key group of 32 keeps its K and V in registers and walks the 32-query
 //     tiles of the group's query heads (Q, dO and the row statistics copied
@@ -63,25 +64,41 @@ struct BwdParams {
 constexpr int kBwdRows = 32;  // rows of a staged tile (queries or keys)
 
 // ---------------------------------------------------------------- delta
+// A row's 16-byte chunks are spread over kDeltaLanes<D> adjacent lanes, so
+// each load instruction reads whole rows (coalesced); the lanes' partial dot
+// products are then summed across the group.
+template <int D>
+constexpr int kDeltaLanes = D / 8 <= 8 ? 8 : 16;
+template <int D>
+constexpr int kDeltaRowsPerBlock = 4 * (64 / kDeltaLanes<D>);
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
-  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (row >= (int64_t)p.B * p.Hq * p.Lq) return;
-  const int i = (int)(row % p.Lq);
-  const int64_t bh = row / p.Lq;
-  const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
-  const uint16_t* orow = reinterpret_cast<const uint16_t*>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)i * p.o_st;
-  const uint16_t* drow =
-      reinterpret_cast<const uint16_t*>(p.dout) + b * p.do_sb + h * p.do_sh + (int64_t)i * p.do_st;
+  constexpr int C = D / 8;  // 16-byte chunks of a row
+  constexpr int LPR = kDeltaLanes<D>;
+  static_assert(C <= LPR, "a row's chunks fit its lane group");
+  const int lane = threadIdx.x & 63;
+  const int sub = lane % LPR;
+  const int64_t nrows = (int64_t)p.B * p.Hq * p.Lq;
+  const int64_t row = (int64_t)blockIdx.x * kDeltaRowsPerBlock<D> + (threadIdx.x >> 6) * (64 / LPR) + lane / LPR;
   float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const u32x4 a = load16(orow + 8 * c), d = load16(drow + 8 * c);
+  if (row < nrows && sub < C) {
+    const int i = (int)(row % p.Lq);
+    const int64_t bh = row / p.Lq;
+    const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
+    const u32x4 a = load16(reinterpret_cast<const uint16_t*>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)i * p.o_st +
+                           8 * sub);
+    const u32x4 d = load16(reinterpret_cast<const uint16_t*>(p.dout) + b * p.do_sb + h * p.do_sh +
+                           (int64_t)i * p.do_st + 8 * sub);
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc += bf16_lo(a[e]) * bf16_lo(d[e]) + bf16_hi(a[e]) * bf16_hi(d[e]);
   }
-  p.stats[2 * row] = p.lse[row] * kLog2e;
-  p.stats[2 * row + 1] = acc;
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (sub == 0 && row < nrows) {
+    p.stats[2 * row] = p.lse[row] * kLog2e;
+    p.stats[2 * row + 1] = acc;
+  }
 }
 
 // ---------------------------------------------------------------- dK, dV
