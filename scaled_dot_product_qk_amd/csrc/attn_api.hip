@@ -567,7 +567,8 @@ static attn_status_t launch_decode(const DecodeParams& p, int B, hipStream_t s) 
     hipLaunchKernelGGL(attn_decode_split_kernel<D>, dim3(p.n_wg), dim3(256), 0, s, p);
     if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
   }
-  hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3(B * p.Hq), dim3(D), 0, s, p);
+  hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3((unsigned)(((int64_t)B * p.Hq + kDecMergeWaves - 1) / kDecMergeWaves)),
+                     dim3(64 * kDecMergeWaves), 0, s, p);
   return launch_status();
 }
 

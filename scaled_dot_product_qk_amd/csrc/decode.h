@@ -33,7 +33,7 @@
 // instruction) and transposes them with byte permutes, so O^T row m of the
 // product number t is head_dim index 8m + t.  No LDS is used on the way.
 //
-// Merge kernel: one workgroup per (b, query head) combines the pieces with the
+// Merge kernel: one wave per (b, query head) combines the pieces with the
 // cnblogs section 四 identity on (O_s, LSE_s) pairs:
 //   M = max_s LSE_s,  LSE = M + ln sum_s e^(LSE_s - M),
 //   O = sum_s e^(LSE_s - LSE) O_s.
@@ -132,12 +132,6 @@ __device__ __forceinline__ void dec_find(const DecodeParams& p, int lane, int y,
   }
 }
 
-// First position of sequence b in the lengths laid end to end.
-__device__ __forceinline__ int dec_prefix(const DecodeParams& p, int lane, int b) {
-  int s = 0;
-  for (int b0 = 0; b0 < b; b0 += 64) s += wave_sum_i32(b0 + lane < b ? dec_len(p, b0 + lane) : 0);
-  return __builtin_amdgcn_readfirstlane(s);
-}
 
 template <int D>
 __global__ __launch_bounds__(256, kDecGroupsPerCU) void attn_decode_split_kernel(DecodeParams p) {
@@ -350,57 +344,84 @@ __global__ __launch_bounds__(256, kDecGroupsPerCU) void attn_decode_split_kernel
   }
 }
 
+// Merge: one wave per (sequence, query head), D / 64 head_dim values per
+// lane; four (sequence, head) pairs per workgroup.
+constexpr int kDecMergeWaves = 4;
+
 template <int D>
-__global__ __launch_bounds__(D) void attn_decode_merge_kernel(DecodeParams p) {
-  const int bh = blockIdx.x;
-  const int b = bh / p.Hq;
-  const int h = bh - b * p.Hq;
-  const int d = threadIdx.x;
-  const int lane = d & 63;
-  // The pieces of unit (kv head, head group) of sequence b: those holding
-  // its slots [u * total + pre, u * total + pre + L).
-  const int L = dec_len(p, b);
+__global__ __launch_bounds__(64 * kDecMergeWaves) void attn_decode_merge_kernel(DecodeParams p) {
+  constexpr int E = D / 64;  // head_dim values per lane
+  static_assert(E * 64 == D, "merge lanes cover head_dim exactly");
+  const int lane = threadIdx.x & 63;
+  const int64_t bh = (int64_t)blockIdx.x * kDecMergeWaves + (threadIdx.x >> 6);
+  if (bh >= (int64_t)p.B * p.Hq) return;  // whole wave leaves together
+  const int b = (int)(bh / p.Hq);
+  const int h = (int)(bh - (int64_t)b * p.Hq);
+  // One pass over the lengths gives this sequence's length, its first
+  // position and the total.  The pieces of unit (kv head, head group) of
+  // sequence b are those holding its slots [u * total + pre, u * total + pre + L).
+  int L = 0, pre = 0, total = 0;
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const int len = b0 + lane < p.B ? dec_len(p, b0 + lane) : 0;
+    total += wave_sum_i32(len);
+    pre += wave_sum_i32(b0 + lane < b ? len : 0);
+    if (b >= b0 && b < b0 + 64) L = __builtin_amdgcn_readlane(len, b - b0);
+  }
   int ns = 0;
   if (L > 0) {
-    const int total = dec_total(p, lane);
-    const int pre = dec_prefix(p, lane, b);
     const int64_t S = dec_piece((int64_t)p.Hkv * p.n_hgroups * total, p.n_wg);
     const int hkv = h / p.group;
     const int u = hkv * p.n_hgroups + (h - hkv * p.group) / kDecHeadsPerGroup;
     const int64_t first = (int64_t)u * total + pre;
     ns = (int)((first + L - 1) / S - first / S + 1);
   }
-  const int64_t row0 = (int64_t)bh * p.n_pieces;
+  const int64_t row0 = bh * p.n_pieces;
 
-  // Up to 16 pieces per pass, their loads issued together; the running max
+  // Up to 8 pieces per pass, their loads issued together; the running max
   // and sums are rescaled between passes.
-  float M = kNegInf, wsum = 0.f, acc = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += 16) {
-    float lsv[16], ov[16];
+  constexpr int kPass = 8;
+  float M = kNegInf, wsum = 0.f, acc[E];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += kPass) {
+    float lsv[kPass], ov[kPass][E];
+#pragma unroll
+    for (int j = 0; j < kPass; ++j) {
       const bool ok = s0 + j < ns;
       lsv[j] = ok ? p.lse_part[row0 + s0 + j] : kNegInf;
-      ov[j] = ok ? p.o_part[(row0 + s0 + j) * D + d] : 0.f;
+      const float* src = p.o_part + (row0 + s0 + j) * D + E * lane;
+      if constexpr (E == 2) {
+        const f32x2 v = ok ? *reinterpret_cast<const f32x2*>(src) : f32x2{0.f, 0.f};
+        ov[j][0] = v[0];
+        ov[j][1] = v[1];
+      } else {
+        ov[j][0] = ok ? src[0] : 0.f;
+      }
     }
     float Mc = M;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) Mc = fmaxf(Mc, lsv[j]);
+    for (int j = 0; j < kPass; ++j) Mc = fmaxf(Mc, lsv[j]);
     const float sc = expf(M - Mc);  // first pass: exp(-inf) = 0 on zero sums
     wsum *= sc;
-    acc *= sc;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int e = 0; e < E; ++e) acc[e] *= sc;
+#pragma unroll
+    for (int j = 0; j < kPass; ++j) {
       const float w = expf(lsv[j] - Mc);
       wsum += w;
-      acc += w * ov[j];
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += w * ov[j][e];
     }
     M = Mc;
   }
-  const float o = ns > 0 ? acc / wsum : 0.f;
   uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + b * p.o_sb + (int64_t)h * p.o_sh;
-  orow[d] = (uint16_t)(pack_bf16x2(o, 0.f) & 0xffffu);  // bf16, round-to-nearest-even
-  if (d == 0) p.lse[bh] = ns > 0 ? M + logf(wsum) : kNegInf;
+  const float inv = ns > 0 ? 1.f / wsum : 0.f;
+  if constexpr (E == 2) {
+    *reinterpret_cast<uint32_t*>(orow + 2 * lane) = pack_bf16x2(acc[0] * inv, acc[1] * inv);  // bf16, RNE
+  } else {
+    orow[lane] = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.f) & 0xffffu);
+  }
+  if (lane == 0) p.lse[bh] = ns > 0 ? M + logf(wsum) : kNegInf;
 }
 
 }  // namespace attn_dev
