@@ -116,6 +116,27 @@ def test_empty_query_is_noop(dev):
     assert o.numel() == 0 and lse.numel() == 0
 
 
+@pytest.mark.parametrize("d", [64, 80, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_output_rows_past_lq_untouched(dev, d, causal):
+    """The epilogue stores whole rows (staged through LDS at d = 64 and 128):
+    with Lq = 200 the last query tile holds rows past Lq, and O is a view into
+    a larger buffer whose other rows and heads carry a sentinel that must
+    survive."""
+    B, Hq, Hkv, L = 2, 4, 2, 200
+    w = wl.FwdWorkload("rows_past_lq", B, Hq, Hkv, L, L, d, "bf16", causal, 1700 + d)
+    q, k, v = wl.make_fwd_inputs(w)
+    sentinel = -7.0
+    big = torch.full((B, Hq + 1, L + 64, d), sentinel, dtype=torch.bfloat16, device=dev)
+    out = big[:, 1:, :L]
+    o, lse = sdpa.attn_fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal, out=out)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = orc.attention_forward(q, k, v, causal=causal)
+    check(to_np(out), o_ref, to_np(lse), lse_ref, "bf16", f"rows past Lq d{d} causal={causal}")
+    assert (big[:, 0] == sentinel).all().item()
+    assert (big[:, 1:, L:] == sentinel).all().item()
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_strided_layouts(dev, causal):
     """[B, L, H, d] storage viewed as [B, H, L, d]; output into a strided view."""
