@@ -498,11 +498,13 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) s[nb][sb] = mfma32(ka[kc], qop[nb][kc], s[nb][sb]);
   };
+  // (the 16-key slices j outermost, so that consecutive products accumulate
+  // into different output blocks even with one row block per wave)
   auto pv = [&](int sb, const u32x4 (&va)[S::kND][2]) {
 #pragma unroll
-    for (int db = 0; db < S::kND; ++db)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int db = 0; db < S::kND; ++db)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) oacc[nb][db] = mfma32(va[db][j], pop[nb][2 * sb + j], oacc[nb][db]);
   };
