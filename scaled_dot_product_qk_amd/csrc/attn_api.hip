@@ -564,7 +564,7 @@ extern "C" attn_status_t attn_validate_decode(const attn_decode_args_t* a) {
 template <int D>
 static attn_status_t launch_decode(const DecodeParams& p, int B, hipStream_t s) {
   if (p.Lmax > 0) {
-    hipLaunchKernelGGL(attn_decode_split_kernel<D>, dim3(p.n_wg), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attn_decode_split_kernel<D>, dim3(p.n_wg), dim3(64 * kDecWaves), 0, s, p);
     if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
   }
   hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3((unsigned)(((int64_t)B * p.Hq + kDecMergeWaves - 1) / kDecMergeWaves)),
@@ -600,7 +600,7 @@ extern "C" attn_status_t attn_decode(const attn_decode_args_t* a, void* workspac
   p.B = (int)a->B;
   p.n_hgroups = (p.group + kDecHeadsPerGroup - 1) / kDecHeadsPerGroup;
   p.n_pieces = (int)decode_pieces(a->Lmax);
-  // One piece per resident split workgroup, fewer when even the largest
+  // One piece per split workgroup, fewer when even the largest
   // possible total (every sequence at Lmax) would leave pieces below the minimum.
   {
     const int64_t most = (a->Hkv * p.n_hgroups * a->B * a->Lmax + kDecMinPiece - 1) / kDecMinPiece;

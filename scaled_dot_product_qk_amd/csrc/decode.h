@@ -12,18 +12,21 @@
 // 16 query heads sharing it); every sequence b contributes L_b slots to each
 // unit.  The slots are laid end to end, unit class by unit class and, within
 // one, sequence by sequence, and the whole range is cut into n_wg equal pieces
-// of S slots, one per workgroup of the split kernel (n_wg is a few
-// workgroups per compute unit, so all of them are resident together and
-// finish together whatever the mix of lengths).  A piece may cover the end of
+// of S slots, one per workgroup of the split kernel (n_wg is one workgroup
+// of two waves per compute unit, so all of them are resident together and
+// finish together whatever the mix of lengths; the cache reads are
+// non-temporal, and fewer concurrent streams read HBM faster: two waves per
+// compute unit measured above three or four, and one workgroup per compute
+// unit above two).  A piece may cover the end of
 // one (sequence, unit) and the start of the next; each such segment yields one
 // partial (O_s, LSE_s) per query head.  The lengths live on the device, so
 // every workgroup derives S and its segments from them (a prefix sum over the
 // sequences in each wave).  Slots at or beyond a sequence's length are never
 // loaded.
 //
-// Within a segment the 4 waves take equal shares and walk them 32 keys at a
+// Within a segment the waves take equal shares and walk them 32 keys at a
 // time with the tiled online softmax of the cnblogs page's sections 三-四;
-// the 4 partial results are combined in LDS and written to the workspace.
+// their partial results are combined in LDS and written to the workspace.
 //
 // Matrix-core use: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with the 16 keys on
 // the M side and the query heads of the group on the N side; O^T = V^T P^T on
@@ -44,9 +47,9 @@
 namespace attn_dev {
 
 constexpr int kDecMinPiece = 512;              // fewest cache slots per split workgroup
-constexpr int kDecWaves = 4;
+constexpr int kDecWaves = 2;
 constexpr int kDecHeadsPerGroup = 16;
-constexpr int kDecGroupsPerCU = 3;             // resident split workgroups per compute unit
+constexpr int kDecGroupsPerCU = 1;             // split workgroups (pieces) per compute unit
 
 struct DecodeParams {
   const void* q;
@@ -134,7 +137,7 @@ __device__ __forceinline__ void dec_find(const DecodeParams& p, int lane, int y,
 
 
 template <int D>
-__global__ __launch_bounds__(256, kDecGroupsPerCU) void attn_decode_split_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64 * kDecWaves, kDecGroupsPerCU) void attn_decode_split_kernel(DecodeParams p) {
   static_assert(D % 32 == 0 && D <= 128, "decode head_dim must be 32, 64, 96 or 128");
   constexpr int KC = D / 32;      // k-slices of S^T = K Q^T
   __shared__ float red_m[kDecWaves][16];
@@ -175,7 +178,7 @@ __global__ __launch_bounds__(256, kDecGroupsPerCU) void attn_decode_split_kernel
     const uint16_t* kg = reinterpret_cast<const uint16_t*>(p.k) + b * p.k_sb + hkv * p.k_sh;
     const uint16_t* vg = reinterpret_cast<const uint16_t*>(p.v) + b * p.v_sb + hkv * p.v_sh;
 
-    // equal shares of whole 32-key steps for the 4 waves
+    // equal shares of whole 32-key steps for the waves
     const int share = (k1 - k0 + 32 * kDecWaves - 1) / (32 * kDecWaves) * 32;
     const int w0 = k0 + wave * share;
     const int w1 = min(w0 + share, k1);
@@ -289,7 +292,7 @@ __global__ __launch_bounds__(256, kDecGroupsPerCU) void attn_decode_split_kernel
       load_v(nxt, vreg);
     }
 
-    // Combine the 4 waves' partial results in LDS.
+    // Combine the waves' partial results in LDS.
     const float l_wave = sum_xor32(sum_xor16(l_run));
     if (g == 0) {
       red_m[wave][n] = m_run;
@@ -305,7 +308,7 @@ __global__ __launch_bounds__(256, kDecGroupsPerCU) void attn_decode_split_kernel
     __syncthreads();
 
     const int64_t part_row0 = ((int64_t)b * p.Hq + hkv * p.group + kDecHeadsPerGroup * hg) * p.n_pieces;
-    for (int idx = tid; idx < 16 * D; idx += 256) {
+    for (int idx = tid; idx < 16 * D; idx += 64 * kDecWaves) {
       const int col = idx / D;
       const int d = idx - col * D;
       if (kDecHeadsPerGroup * hg + col >= p.group) continue;
