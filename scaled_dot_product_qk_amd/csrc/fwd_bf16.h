@@ -730,6 +730,18 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) va_last[db][j] = zero16();
     if (active(0)) qk(0, ka_next);
+    // With no key of tile 0 past Lk, the reference starts at the first half's
+    // row max (no key is masked here), so tile 0 does not take the exact
+    // path that a reference of -inf would force on both of its halves.
+    if (n_plain > 0) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][0][r]);
+        m_run[nb] = max_xor32(mx) * c;  // the scale is positive
+      }
+    }
     // Phase A of tile t (the wave is active there).  The V^T operands of the
     // first half are read at its end, before the barrier; those of the
     // second half at the end of phase B (the buffer of tile t is refilled
