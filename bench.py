@@ -9,9 +9,10 @@ the step as a whole is timed with host clocks between device synchronisations.
 After the step loop, attn_fwd_varlen on 16 packed causal GQA sequences of
 256..4096 tokens (d=128), attn_bwd on the causal GQA n=8192 d=128 workload,
 attn_fwd_masked on the n=4096 d=64 workload with one boolean mask shared by
-all heads, and attn_fwd_fp8 on e4m3 versions of the two prefill workloads are
-timed the same way, each on its own, and reported in `extra` (they are not
-part of the step).
+all heads, attn_fwd_fp8 on e4m3 versions of the two prefill workloads, and
+the headline shape at n = 2048, 4096 and 8192 (the time should grow 4x per
+doubling of n) are timed the same way, each on its own, and reported in
+`extra` (they are not part of the step).
 
 Prints ONE JSON line.  `value` is the headline workload's attention-forward
 throughput in TFLOP/s (credited flops 4 n^2 d H B, halved when causal).
@@ -76,7 +77,7 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--only", choices=["all", "fwd_n4096", "fwd_causal_n8192", "decode", "fwd_varlen", "bwd",
+    ap.add_argument("--only", choices=["all", "fwd_n4096", "fwd_causal_n8192", "decode", "fwd_varlen", "bwd", "fwd_scaling",
                                        "fwd_masked", "fwd_fp8_n4096", "fwd_fp8_causal_n8192"],
                     default="all",
                     help="time one call of the step only (profiling runs)")
@@ -131,10 +132,11 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
 
-    SOLO = ("fwd_varlen", "bwd", "fwd_masked", "fwd_fp8_n4096", "fwd_fp8_causal_n8192")
+    SOLO = ("fwd_varlen", "bwd", "fwd_masked", "fwd_fp8_n4096", "fwd_fp8_causal_n8192", "fwd_scaling_2048",
+            "fwd_scaling_4096", "fwd_scaling_8192")
     names = ["fwd_n4096", "fwd_causal_n8192", "decode"] if args.only == "all" else \
-        ([] if args.only in SOLO else [args.only])
-    solo = [n for n in SOLO if args.only in ("all", n)]
+        ([] if args.only in SOLO or args.only == "fwd_scaling" else [args.only])
+    solo = [n for n in SOLO if args.only in ("all", n) or (args.only == "fwd_scaling" and n.startswith("fwd_scaling"))]
     with_varlen, with_bwd, with_masked = ("fwd_varlen" in solo), ("bwd" in solo), ("fwd_masked" in solo)
 
     # ---- inputs, generated on the host and copied once to HBM ----
@@ -198,6 +200,18 @@ def main():
             fp8_in[n] = (w, G8)
             calls[n] = (lambda G8=G8, ds8=ds8, o8=o8, l8=l8, c=w.causal:
                         sdpa.attn_fwd_fp8(*G8, ds8, causal=c, out=o8, lse=l8, stream=stream))
+    # the headline shape at n = 2048, 4096, 8192: time should grow 4x per doubling of n
+    scal = {}
+    for n_s in (2048, 4096, 8192):
+        nm = f"fwd_scaling_{n_s}"
+        if nm in solo:
+            ws_ = wl.FwdWorkload(f"fwd_bf16_b1_h96_n{n_s}_d64", 1, 96, 96, n_s, n_s, 64, "bf16", False, 1020 + n_s)
+            GS = [t.to(dev) for t in wl.make_fwd_inputs(ws_)]
+            os_ = torch.empty_like(GS[0])
+            ls_ = torch.empty(GS[0].shape[:3], dtype=torch.float32, device=dev)
+            scal[nm] = ws_
+            calls[nm] = (lambda GS=GS, os_=os_, ls_=ls_:
+                         sdpa.attn_fwd(*GS, causal=False, out=os_, lse=ls_, stream=stream))
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -284,6 +298,16 @@ def main():
                       + w.B * w.Hq * w.Lq * w.d,  # O is bf16: one more byte per element
                       "workload": w.name}
 
+    if scal and all(n in ms for n in scal):
+        ns_ = sorted(scal, key=lambda n: scal[n].Lq)
+        ts = [ms[n] for n in ns_]
+        res["fwd_scaling"] = {
+            "workload": "fwd_bf16_b1_h96_d64 (non-causal), each n timed on its own",
+            "n": [scal[n].Lq for n in ns_], "ms": ts,
+            "tflops": [wl.algorithmic_flops_fwd(1, 96, scal[n].Lq, scal[n].Lk, 64, False) / (ms[n] / 1e3) / 1e12
+                       for n in ns_],
+            "time_ratio_per_doubling": [ts[i + 1] / ts[i] for i in range(len(ts) - 1)]}
+
     def roof_fwd(r, tag, peak=PEAK_BF16_TFLOPS):
         tr = counted_traffic(tag)
         return {"bound": "mfma", "achieved": r["tflops"], "peak": peak, "unit": "TFLOP/s",
@@ -332,6 +356,8 @@ def main():
         r = res["fwd_fp8_causal_n8192"]
         out["extra"]["fwd_fp8_causal_gqa_n8192_d128"] = dict(
             r, roofline=roof_fwd(r, "attn_fwd_fp8_d128_causal_n8192", PEAK_FP8_TFLOPS))
+    if "fwd_scaling" in res:
+        out["extra"]["fwd_scaling_n2048_4096_8192_d64"] = res["fwd_scaling"]
     if headline:
         out["extra"]["fwd_n4096_d64"] = headline
     if not args.no_cpu_baseline and args.only in ("all", "fwd_n4096"):
