@@ -402,26 +402,6 @@ def merge_partials(o_parts, lse_parts):
     return o, lse
 
 
-def softmax_two_blocks(x: np.ndarray):
-    """Row softmax of x [..., n] from two key blocks' own statistics.
-
-    The cnblogs page's section 四 derivation: each block keeps its own maximum
-    m_i and exponent sum e_i; the global maximum is m = max(m_1, m_2), the
-    normaliser is e_1 exp(m_1 - m) + e_2 exp(m_2 - m), and each block's
-    weights are exp(x - m) / l.  Computed in x's dtype.
-    """
-    n = x.shape[-1]
-    mid = n // 2
-    x1, x2 = x[..., :mid], x[..., mid:]
-    m1 = x1.max(axis=-1, keepdims=True)
-    m2 = x2.max(axis=-1, keepdims=True)
-    m = np.maximum(m1, m2)
-    e1 = np.exp(x1 - m1).sum(axis=-1, keepdims=True)
-    e2 = np.exp(x2 - m2).sum(axis=-1, keepdims=True)
-    l = e1 * np.exp(m1 - m) + e2 * np.exp(m2 - m)
-    return np.concatenate([np.exp(x1 - m) / l, np.exp(x2 - m) / l], axis=-1)
-
-
 def brute_force_attention(q, k, v, causal: bool = False, scale: Optional[float] = None,
                           n_keys: Optional[Sequence[int]] = None, mask=None):
     """Per-element pure-Python evaluation for tiny shapes (no numpy arithmetic).

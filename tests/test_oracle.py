@@ -177,20 +177,36 @@ def test_merge_all_empty_parts():
     assert (o == 0).all() and np.isneginf(l).all()
 
 
-def test_two_block_softmax_page_demo():
-    """The online-softmax demo: randn(2, 512, 4096) * 2 split into two key
-    blocks; the page expects agreement near machine precision (1e-6) in fp32."""
+def test_two_key_blocks_merged_reproduce_page_demo():
+    """The online-softmax demo: scores randn(2, 512, 4096) * 2 split into two
+    key blocks; the page expects the blockwise result to agree with the
+    standard softmax near machine precision (1e-6) in fp32.
+
+    Each block is run through the oracle's own attention with unit keys and
+    values (key j and value j are the j-th unit vector, scale 1), so that a
+    query whose d-vector is its score row has exactly those scores and its
+    output row is its probability row.  The two blocks' (O, LSE) pairs are
+    merged with merge_partials: in float32, as the page's demo runs, against
+    torch's float32 softmax; in float64 against torch's float64 softmax."""
     fig = json.load(open(GOLDEN))["online_softmax_demo"]
     x = torch.randn(*fig["shape"], generator=torch.Generator().manual_seed(0)) * fig["x_scale"]
-    x32 = x.numpy()
-    ref32 = torch.softmax(x, dim=-1).numpy()
-    got32 = orc.softmax_two_blocks(x32)
-    assert got32.dtype == np.float32
-    assert np.abs(got32 - ref32).max() <= 10 * fig["max_abs_diff_fp32_order"]
-    x64 = x32.astype(np.float64)
-    ref64 = np.exp(x64 - x64.max(-1, keepdims=True))
-    ref64 /= ref64.sum(-1, keepdims=True)
-    assert np.abs(orc.softmax_two_blocks(x64) - ref64).max() <= 1e-15
+    B, R, n = x.shape
+    mid = n // 2
+    q = x.numpy().astype(np.float64)[:, None]  # [B, 1, R, n]
+    eye = np.eye(n)
+    parts = []
+    for a, b in ((0, mid), (mid, n)):
+        kv = np.broadcast_to(eye[a:b], (B, 1, b - a, n))
+        parts.append(orc.attention_forward(q, kv, kv, scale=1.0))
+    o32, l32 = orc.merge_partials([p[0].astype(np.float32) for p in parts],
+                                  [p[1].astype(np.float32) for p in parts])
+    assert o32.dtype == np.float32
+    ref32 = torch.softmax(x, dim=-1).numpy()[:, None]
+    assert np.abs(o32 - ref32).max() <= 10 * fig["max_abs_diff_fp32_order"]
+    o64, l64 = orc.merge_partials([p[0] for p in parts], [p[1] for p in parts])
+    x64 = x.double()
+    assert np.abs(o64 - torch.softmax(x64, dim=-1).numpy()[:, None]).max() <= 1e-15
+    assert np.abs(l64 - torch.logsumexp(x64, dim=-1).numpy()[:, None]).max() <= 1e-12
 
 
 # ------------------------------------------ P-11 large score magnitudes
