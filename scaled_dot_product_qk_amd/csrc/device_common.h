@@ -101,6 +101,13 @@ __device__ __forceinline__ void lds_copy4(const void* base, uint32_t off, uint32
   asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_base) : "memory");
 }
 
+// Marks the end of one group of copies in the assembly (an assembler
+// comment; no instruction).  A kernel that waits with vmcnt(N) for all but
+// its last group of N copies relies on every group issuing exactly N copy
+// instructions on every way through the code; the marker lets a CPU test
+// of the compiled code count them per group.
+__device__ __forceinline__ void copy_group_end() { asm volatile(";;#copy-group-end"); }
+
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

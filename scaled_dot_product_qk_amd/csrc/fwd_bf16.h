@@ -319,8 +319,13 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
   // row l / kPitch, physical chunk l % kPitch) of the K tile (first half of
   // the ci range) or the V tile; wave w issues kCopiesPerWave consecutive
   // ones, so waves 0-1 copy K and waves 2-3 copy V.  Each lane fetches the
-  // logical chunk its slot holds; slots of padding chunks (head_dim 80) stay
-  // idle.  Per-lane offsets repeat with period kKVar copies.
+  // logical chunk its slot holds.  A slot of a padding chunk (head_dim 80:
+  // chunks 10-15 of a 16-chunk LDS row) fetches chunk c - 8 of its row
+  // instead, which a lane of the same instruction already requests: no K
+  // read touches the padding, and the V^T rows it feeds are discarded.  So
+  // every lane copies and each issue_tile issues exactly kCopiesPerWave
+  // copy instructions on every path, which the vmcnt waits below count on.
+  // Per-lane offsets repeat with period kKVar copies.
   constexpr int kHalfCopies = S::kCopies / 2;
   const bool copies_k = wave < S::kWaves / 2;
   const uint16_t* cp_src = copies_k ? kg : vg;
@@ -328,18 +333,19 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
   const int cp_row = lane / S::kPitch;  // row within one copy
   const int cp_row0 = S::kRowsPerCopy * ((wave % (S::kWaves / 2)) * S::kCopiesPerWave);
   const uint32_t cp_lds0 = (uint32_t)(uintptr_t)lds_b + (copies_k ? 0 : S::kTileBytes) + cp_row0 * S::kRowBytes;
-  int cp_chunk16[S::kKVar];   // byte offset of the lane's logical chunk
-  uint32_t cp_off[S::kKVar];  // byte offset of the lane's chunk within its copy
-  bool cp_on[S::kKVar];
+  int cp_chunk16[S::kKVar];   // byte offset of the chunk the lane fetches
+  uint32_t cp_off[S::kKVar];  // byte offset of that chunk within its copy
   const uint32_t cp_row_bytes = (uint32_t)(2 * cp_st);  // < 2^29: token strides are validated
+  static_assert(S::kChunks == S::kPitch || (S::kChunks >= 8 && S::kPitch - 8 <= S::kChunks),
+                "a padding slot's stand-in chunk c - 8 is a real chunk of the row");
 #pragma unroll
   for (int v = 0; v < S::kKVar; ++v) {
     const int r = S::kRowsPerCopy * v + cp_row;  // row index modulo the swizzle period
     const int pc = lane % S::kPitch;
-    const int lc = pc ^ (copies_k ? fwd_k_swz<S::kPitch>(r) : fwd_v_swz<S::kPitch>(r));
+    int lc = pc ^ (copies_k ? fwd_k_swz<S::kPitch>(r) : fwd_v_swz<S::kPitch>(r));
+    if (lc >= S::kChunks) lc -= 8;  // padding slot
     cp_chunk16[v] = 16 * lc;
     cp_off[v] = (uint32_t)cp_row * cp_row_bytes + 16 * lc;
-    cp_on[v] = lc < S::kChunks;
   }
   // Mask copy plan: wave w fills mask-tile rows m_row0 .. m_row0 +
   // MS::kCopiesPerWave * MS::kRowsPerCopy - 1; lane l -> row l / chunks-per-row,
@@ -366,8 +372,7 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
 #pragma unroll
       for (int j = 0; j < S::kCopiesPerWave; ++j) {
         const uint16_t* src = cp_src + (int64_t)(kv0 + cp_row0 + S::kRowsPerCopy * j) * cp_st;
-        if (S::kChunks == S::kPitch || cp_on[j % S::kKVar])
-          fwd_copy16(src, cp_off[j % S::kKVar], dst + j * S::kRowsPerCopy * S::kRowBytes);
+        fwd_copy16(src, cp_off[j % S::kKVar], dst + j * S::kRowsPerCopy * S::kRowBytes);
       }
     } else {
       const int last = p.Lk - 1;
@@ -375,9 +380,8 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
       for (int j = 0; j < S::kCopiesPerWave; ++j) {
         const int row0 = min(kv0 + cp_row0 + S::kRowsPerCopy * j, last);
         const int row = min(kv0 + cp_row0 + S::kRowsPerCopy * j + cp_row, last);
-        if (S::kChunks == S::kPitch || cp_on[j % S::kKVar])
-          fwd_copy16(cp_src + (int64_t)row0 * cp_st, (uint32_t)(row - row0) * cp_row_bytes + cp_chunk16[j % S::kKVar],
-                     dst + j * S::kRowsPerCopy * S::kRowBytes);
+        fwd_copy16(cp_src + (int64_t)row0 * cp_st, (uint32_t)(row - row0) * cp_row_bytes + cp_chunk16[j % S::kKVar],
+                   dst + j * S::kRowsPerCopy * S::kRowBytes);
       }
     }
     if constexpr (MK != 0) {
@@ -395,6 +399,7 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
                    mdst + (m_row0 + MS::kRowsPerCopy * j) * MS::kRowBytes);
       }
     }
+    copy_group_end();
   };
 
   // ---- LDS operand offsets (bytes within a buffer) ----

@@ -196,6 +196,7 @@ attn_fwd_fp8_kernel(FwdParams p) {
                    dst + j * S::kRowsPerCopy * S::kRowBytes);
       }
     }
+    copy_group_end();
   };
 
   // ---- LDS operand offsets (bytes within a buffer) ----
