@@ -4,12 +4,18 @@ One step = one pass of the whole path over synthetic, HBM-resident inputs:
   1. attn_fwd, non-causal, B=1, H=96, n=4096, d=64, bf16     (headline workload)
   2. attn_fwd, causal GQA, B=1, Hq=32, Hkv=8, n=8192, d=128, bf16
   3. attn_decode, B=64, Hq=32, Hkv=8, d=128, cache lengths U{1024..8192}, bf16
-Each call is timed with HIP events recorded on the stream the kernels run on;
-the step as a whole is timed with host clocks between device synchronisations.
+Each call is timed with HIP events recorded on the stream the kernels run on
+(median, minimum, maximum and mean per call are reported; rates use the
+median); the step as a whole is timed with host clocks between device
+synchronisations.  The host-side cost of a call (argument checks, marshalling
+and the launches, no device synchronisation) is timed separately with a CPU
+clock, through the Python binding and through the bare C entry point.
 After the step loop, attn_fwd_varlen on 16 packed causal GQA sequences of
 256..4096 tokens (d=128), attn_bwd on the causal GQA n=8192 d=128 workload,
 attn_fwd_masked on the n=4096 d=64 workload with one boolean mask shared by
-all heads, attn_fwd_fp8 on e4m3 versions of the two prefill workloads, and
+all heads, attn_fwd_fp8 on e4m3 versions of the two prefill workloads,
+attn_fwd on the causal B=4, H=16, n=2048, d=80 workload (the head size that
+is not a power of two), and
 the headline shape at n = 2048, 4096 and 8192 (the time should grow 4x per
 doubling of n) are timed the same way, each on its own, and reported in
 `extra` (they are not part of the step).
@@ -19,7 +25,10 @@ throughput in TFLOP/s (credited flops 4 n^2 d H B, halved when causal).
 `roofline` covers the headline kernel; the other two calls are reported in
 `extra` with their own rooflines (bf16 matrix peak for prefill, HBM peak for
 decode).  `cpu_baseline` times the CPU oracle on a bounded sample of the
-headline workload.
+headline workload (`value`), and per workload: the fp32 n=256 case, the
+headline, the d=80 causal workload and the decode workload with every host
+thread it may use and on one core, and four query heads of the n=8192 causal
+workload; it records the host's CPU model and core count.
 """
 from __future__ import annotations
 
@@ -27,7 +36,9 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import re
+import statistics
 import sys
 import time
 
@@ -78,11 +89,12 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--only", choices=["all", "fwd_n4096", "fwd_causal_n8192", "decode", "fwd_varlen", "bwd", "fwd_scaling",
-                                       "fwd_masked", "fwd_fp8_n4096", "fwd_fp8_causal_n8192"],
+                                       "fwd_masked", "fwd_fp8_n4096", "fwd_fp8_causal_n8192", "fwd_c3_d80"],
                     default="all",
                     help="time one call of the step only (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=96)
+    ap.add_argument("--no-host-timing", action="store_true", help="skip the host-side cost per call")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -99,20 +111,111 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
 
 
-def cpu_baseline(q, k, v, heads: int):
-    """The CPU oracle (untuned) on `heads` whole heads of the headline workload."""
+def host_info():
+    """The machine the CPU legs run on: logical CPUs, the CPUs this process
+    may use, and the CPU model."""
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = os.cpu_count() or 1
+    return {"nproc": os.cpu_count() or 1, "usable_cpus": usable, "cpu_model": model}
+
+
+def _timed(fn, threads):
+    """Wall time of fn(threads); one thread also pins BLAS to one thread."""
+    from threadpoolctl import threadpool_limits
+    if threads == 1:
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            fn(1)
+            return time.perf_counter() - t0
+    t0 = time.perf_counter()
+    fn(threads)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(q, k, v, heads: int, gpu_ms=None):
+    """The CPU oracle (untuned) on `heads` whole heads of the headline
+    workload (the reported value), then on the other workloads, each on a
+    bounded sample, with every host thread it may use (at most 16) and on
+    one core.  gpu_ms maps a workload to the GPU's median time for the whole
+    workload, for the oracle-to-GPU ratio."""
     from oracle import sdpa_oracle as orc
     import workloads as wl
-    threads = min(os.cpu_count() or 1, heads, 16)  # at most 16 host threads
+    gpu_ms = gpu_ms or {}
+    host = host_info()
+    cap = min(host["usable_cpus"], 16)
+    threads = min(cap, heads)
     idx = list(range(heads))
-    t0 = time.perf_counter()
-    orc.attention_forward(q[:, idx], k[:, idx], v[:, idx], causal=False, threads=threads)
-    dt = time.perf_counter() - t0
+    dt = _timed(lambda t: orc.attention_forward(q[:, idx], k[:, idx], v[:, idx], causal=False, threads=t), threads)
     B, _, L, d = q.shape
     flops = wl.algorithmic_flops_fwd(B, heads, L, L, d, False)
+    per = {}
+
+    def fwd_leg(label, w, inputs, sl, threads_, note):
+        qq, kk, vv = inputs
+        qs, ks, vs = qq[sl[0], sl[1]], kk[sl[0], sl[2]], vv[sl[0], sl[2]]
+        t = _timed(lambda n: orc.attention_forward(qs, ks, vs, causal=w.causal, threads=n), threads_)
+        f = wl.algorithmic_flops_fwd(qs.shape[0], qs.shape[1], w.Lq, w.Lk, w.d, w.causal)
+        r = {"workload": w.name, "sample": note, "threads": threads_, "s": t, "tflops": f / t / 1e12}
+        g = gpu_ms.get(w.name)
+        if g:  # oracle time for the whole workload at this rate, over the GPU's
+            r["oracle_over_gpu"] = (wl.algorithmic_flops_fwd(w.B, w.Hq, w.Lq, w.Lk, w.d, w.causal) / f * t) / (g / 1e3)
+        per[label] = r
+
+    per["fwd_n4096_d64"] = {"workload": wl.C2.name, "sample": f"{heads} of 96 heads", "threads": threads, "s": dt,
+                            "tflops": flops / dt / 1e12}
+    if gpu_ms.get(wl.C2.name):
+        per["fwd_n4096_d64"]["oracle_over_gpu"] = (dt * 96 / heads) / (gpu_ms[wl.C2.name] / 1e3)
+    all_ = slice(None)
+    c1 = wl.make_fwd_inputs(wl.C1)
+    fwd_leg("fwd_f32_n256_d64_1core", wl.C1, c1, (all_, all_, all_), 1, "whole workload")
+    c3 = wl.make_fwd_inputs(wl.C3)
+    fwd_leg("fwd_causal_n2048_d80", wl.C3, c3, (all_, all_, all_), cap, "whole workload (64 heads)")
+    fwd_leg("fwd_causal_n2048_d80_1core", wl.C3, c3, (slice(0, 1), all_, all_), 1, "batch 0 (16 of 64 heads)")
+    del c3
+    c4 = wl.make_fwd_inputs(wl.C4)
+    fwd_leg("fwd_causal_gqa_n8192_d128", wl.C4, c4, (all_, slice(0, 4), slice(0, 1)), min(cap, 4),
+            "query heads 0-3 (kv head 0) of 32")
+    del c4
+    qd, kc, vc, lens = wl.make_decode_inputs(wl.C5)
+    ln = lens.numpy()
+    bd = wl.algorithmic_bytes_decode(lens.tolist(), wl.C5.Hq, wl.C5.Hkv, wl.C5.d, 2, wl.C5.Lmax)
+    for label, thr, batches in (("decode_b64_d128", cap, range(wl.C5.B)), ("decode_b64_d128_1core", 1, range(16))):
+        sub = wl.algorithmic_bytes_decode([int(ln[b]) for b in batches], wl.C5.Hq, wl.C5.Hkv, wl.C5.d, 2, wl.C5.Lmax)
+        t = _timed(lambda n: orc.attention_decode(qd, kc, vc, ln, threads=n, batches=list(batches)), thr)
+        r = {"workload": wl.C5.name, "sample": f"{len(batches)} of 64 sequences", "threads": thr, "s": t,
+             "gbps": sub / t / 1e9}
+        if gpu_ms.get(wl.C5.name):
+            r["oracle_over_gpu"] = (bd / sub * t) / (gpu_ms[wl.C5.name] / 1e3)
+        per[label] = r
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{heads} of 96 heads (all 4096 rows each) of the n=4096 d=64 workload, "
-                      f"float64 numpy, {dt:.2f} s wall"}
+                      f"float64 numpy, {threads} threads, {dt:.2f} s wall",
+            "host": host, "per_workload": per}
+
+
+def host_cost_us(fn, n=40):
+    """Median, minimum and maximum host time (us) of fn(), which enqueues
+    device work and returns; the device is idle before each call."""
+    import torch
+    ts = []
+    for _ in range(n):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn()
+        ts.append((time.perf_counter() - t0) * 1e6)
+    torch.cuda.synchronize()
+    return {"median": statistics.median(ts), "min": min(ts), "max": max(ts), "calls": n}
 
 
 def main():
@@ -132,8 +235,8 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
 
-    SOLO = ("fwd_varlen", "bwd", "fwd_masked", "fwd_fp8_n4096", "fwd_fp8_causal_n8192", "fwd_scaling_2048",
-            "fwd_scaling_4096", "fwd_scaling_8192")
+    SOLO = ("fwd_c3_d80", "fwd_varlen", "bwd", "fwd_masked", "fwd_fp8_n4096", "fwd_fp8_causal_n8192",
+            "fwd_scaling_2048", "fwd_scaling_4096", "fwd_scaling_8192")
     names = ["fwd_n4096", "fwd_causal_n8192", "decode"] if args.only == "all" else \
         ([] if args.only in SOLO or args.only == "fwd_scaling" else [args.only])
     solo = [n for n in SOLO if args.only in ("all", n) or (args.only == "fwd_scaling" and n.startswith("fwd_scaling"))]
@@ -163,6 +266,11 @@ def main():
         ws = torch.empty(sdpa.attn_decode_workspace_bytes(wl.C5.B, wl.C5.Hq, wl.C5.Lmax, wl.C5.d),
                          dtype=torch.uint8, device=dev)
         calls["decode"] = lambda: sdpa.attn_decode(*GD, workspace=ws, out=od, lse=ld, stream=stream)
+    if "fwd_c3_d80" in solo:
+        G3 = [t.to(dev) for t in wl.make_fwd_inputs(wl.C3)]
+        o3 = torch.empty_like(G3[0])
+        l3 = torch.empty(G3[0].shape[:3], dtype=torch.float32, device=dev)
+        calls["fwd_c3_d80"] = lambda: sdpa.attn_fwd(*G3, causal=True, out=o3, lse=l3, stream=stream)
     if with_varlen:
         qv, kv_, vv, cqv, ckv = wl.make_varlen_inputs(wl.C6)
         GV = [t.to(dev) for t in (qv, kv_, vv, cqv, ckv)]
@@ -242,7 +350,25 @@ def main():
             b.record(stream)
             ev[n].append((a, b))
         torch.cuda.synchronize()
-    ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / len(ev[n]) for n in ev}
+    times = {n: [a.elapsed_time(b) for a, b in ev[n]] for n in ev}
+    ms = {n: statistics.median(t) for n, t in times.items()}
+    spread = {n: {"ms_min": min(t), "ms_max": max(t), "ms_mean": sum(t) / len(t), "calls": len(t)}
+              for n, t in times.items()}
+
+    # ---- host-side cost per call: CPU clock around the call, no device sync ----
+    host_us = {}
+    if not args.no_host_timing:
+        raw = {}
+        if "fwd_n4096" in calls:
+            a2 = sdpa.make_fwd_args(*G2, o2, l2, False, None)
+            raw["fwd_n4096"] = lambda: sdpa.lib().attn_fwd(sdpa.ctypes.byref(a2), stream.cuda_stream)
+        if "decode" in calls:
+            ad = sdpa.make_decode_args(*GD, od, ld, None)
+            raw["decode"] = lambda: sdpa.lib().attn_decode(sdpa.ctypes.byref(ad), ws.data_ptr(), ws.numel(),
+                                                           stream.cuda_stream)
+        for n, fn in raw.items():
+            assert fn() == 0
+            host_us[n] = {"python_binding": host_cost_us(calls[n]), "c_abi": host_cost_us(fn)}
 
     # ---- accounting ----
     C2, C4, C5 = wl.C2, wl.C4, wl.C5
@@ -264,6 +390,15 @@ def main():
         res["decode"] = {"kernel": "attn_decode_split_kernel<128> + attn_decode_merge_kernel<128>",
                          "ms": ms["decode"], "gbps": bd / t / 1e9, "algorithmic_bytes": bd,
                          "total_cache_keys": int(lens.sum())}
+
+    if "fwd_c3_d80" in ms:
+        C3 = wl.C3
+        f3 = wl.algorithmic_flops_fwd(C3.B, C3.Hq, C3.Lq, C3.Lk, C3.d, C3.causal)
+        t = ms["fwd_c3_d80"] / 1e3
+        res["fwd_c3_d80"] = {"kernel": sdpa.kernel_name(*G3, causal=True), "ms": ms["fwd_c3_d80"],
+                             "tflops": f3 / t / 1e12, "algorithmic_flops": f3,
+                             "algorithmic_bytes": wl.algorithmic_bytes_fwd(C3.B, C3.Hq, C3.Hkv, C3.Lq, C3.Lk, C3.d, 2),
+                             "workload": C3.name}
 
     if "fwd_varlen" in ms:
         C6 = wl.C6
@@ -308,6 +443,12 @@ def main():
                        for n in ns_],
             "time_ratio_per_doubling": [ts[i + 1] / ts[i] for i in range(len(ts) - 1)]}
 
+    for n, r in res.items():
+        if n in spread:
+            r.update(spread[n])
+        if n in host_us:
+            r["host_us_per_call"] = host_us[n]
+
     def roof_fwd(r, tag, peak=PEAK_BF16_TFLOPS):
         tr = counted_traffic(tag)
         return {"bound": "mfma", "achieved": r["tflops"], "peak": peak, "unit": "TFLOP/s",
@@ -340,6 +481,9 @@ def main():
         out["extra"]["decode_b64_gqa_d128"] = dict(r, roofline={
             "bound": "hbm", "achieved": r["gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": r["gbps"] / PEAK_HBM_GBPS, "traffic": counted_traffic("attn_decode_d128_b64")})
+    if "fwd_c3_d80" in res:
+        r = res["fwd_c3_d80"]
+        out["extra"]["fwd_causal_b4_h16_n2048_d80"] = dict(r, roofline=roof_fwd(r, "attn_fwd_bf16_d80_causal_n2048"))
     if "fwd_varlen" in res:
         r = res["fwd_varlen"]
         out["extra"]["fwd_varlen_causal_gqa_b16_d128"] = dict(r, roofline=roof_fwd(r, "attn_fwd_varlen_d128_causal_b16"))
@@ -361,7 +505,9 @@ def main():
     if headline:
         out["extra"]["fwd_n4096_d64"] = headline
     if not args.no_cpu_baseline and args.only in ("all", "fwd_n4096"):
-        out["cpu_baseline"] = cpu_baseline(q2, k2, v2, args.cpu_sample_heads)
+        gpu_ms = {wl.C2.name: ms.get("fwd_n4096"), wl.C3.name: ms.get("fwd_c3_d80"),
+                  wl.C4.name: ms.get("fwd_causal_n8192"), wl.C5.name: ms.get("decode")}
+        out["cpu_baseline"] = cpu_baseline(q2, k2, v2, args.cpu_sample_heads, gpu_ms)
     print(json.dumps(out), flush=True)
 
 

@@ -317,11 +317,20 @@ attn_status_t attn_validate_fwd_fp8(const attn_fwd_fp8_args_t *args);
 attn_status_t attn_validate_bwd(const attn_bwd_args_t *args);
 attn_status_t attn_validate_decode(const attn_decode_args_t *args);
 
-/* Static, human-readable name of a status code. */
+/* Static, human-readable name of a status code.  The status codes are the
+ * library's answer to the failure "SDPA backend 与 FlashAttention" warns of
+ * in sections 3, 7 and 9: an input the fast kernel cannot take silently
+ * runs on a slower path instead (there, head_dim 80 missing the alignment
+ * the fused kernel needs).  Here such an input is refused with a code the
+ * caller can read and print; no call ever falls back to other arithmetic.
+ * Returns "unknown status" for a value outside attn_status_t. */
 const char *attn_status_str(attn_status_t status);
 
 /* Static name of the kernel attn_fwd would launch for these arguments, or
- * "none" if they are invalid or unsupported.  No device work. */
+ * "none" if they are invalid or unsupported.  No device work.  This is the
+ * check "SDPA backend 与 FlashAttention" section 11 asks for: record which
+ * backend a call actually runs, so that a silent change of kernel shows up
+ * in the logs. */
 const char *attn_kernel_name(const attn_fwd_args_t *args);
 
 /* Library version string. */

@@ -21,7 +21,8 @@ STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_
                 4: "ATTN_ERR_LAYOUT", 5: "ATTN_ERR_UNSUPPORTED", 6: "ATTN_ERR_WORKSPACE",
                 7: "ATTN_ERR_HIP"}
 EXPORTED = ("attn_fwd", "attn_fwd_masked", "attn_fwd_varlen", "attn_fwd_fp8", "attn_bwd",
-            "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_workspace_bytes", "attn_validate_fwd",
+            "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_workspace_bytes",
+            "attn_validate_fwd",
             "attn_validate_fwd_masked", "attn_validate_fwd_varlen", "attn_validate_fwd_fp8",
             "attn_validate_bwd", "attn_validate_decode", "attn_status_str", "attn_kernel_name",
             "attn_version")
@@ -454,7 +455,7 @@ def attn_decode(q, k_cache, v_cache, seqlens, scale: Optional[float] = None, wor
     """O [B,Hq,d] and LSE [B,Hq] of one query token per sequence against a KV cache.
 
     q [B,Hq,d]; k_cache/v_cache [B,Hkv,Lmax,d]; seqlens int32 [B] on the device.
-    workspace: optional uint8 device tensor of attn_decode_workspace_bytes bytes.
+    workspace: optional device tensor (any dtype) of at least attn_decode_workspace_bytes bytes.
     """
     import torch
     if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
@@ -481,7 +482,7 @@ def attn_decode(q, k_cache, v_cache, seqlens, scale: Optional[float] = None, wor
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check_device(q, workspace)
     args = make_decode_args(q, k_cache, v_cache, seqlens, out, lse, scale)
-    st = lib().attn_decode(ctypes.byref(args), workspace.data_ptr(), workspace.numel(),
+    st = lib().attn_decode(ctypes.byref(args), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                            _stream_handle(stream))
     if st != 0:
         raise AttnError(st, "attn_decode")

@@ -131,3 +131,20 @@ def test_workload_decode_full(dev):
     o, lse, o_ref, lse_ref, lens = run_decode(w, dev, poison=True)
     print(f"[parity] decode total keys {int(lens.sum())}", flush=True)
     check(to_np(o), o_ref, to_np(lse), lse_ref, "bf16", w.name)
+
+
+def test_decode_workspace_of_another_dtype(dev):
+    """A caller's workspace is counted in bytes whatever its dtype: a float32
+    tensor of exactly the required bytes is accepted, and the result equals
+    that of the call with the library-sized uint8 workspace."""
+    w = wl.DecodeWorkload("dec_ws", 5, 16, 4, 2100, 128, 1, 2100, "bf16", 83)
+    q, kc, vc, lens = (t.to(dev) for t in wl.make_decode_inputs(w))
+    need = sdpa.attn_decode_workspace_bytes(w.B, w.Hq, w.Lmax, w.d)
+    assert need % 4 == 0
+    ws32 = torch.empty(need // 4, dtype=torch.float32, device=dev)
+    a = sdpa.attn_decode(q, kc, vc, lens, workspace=ws32)
+    b = sdpa.attn_decode(q, kc, vc, lens)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    with pytest.raises(sdpa.AttnError):
+        sdpa.attn_decode(q, kc, vc, lens, workspace=ws32[:-1])
