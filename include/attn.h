@@ -74,8 +74,15 @@ typedef enum {
                                group size outside the supported set, sizes past
                                the documented limits) */
   ATTN_ERR_WORKSPACE = 6,   /* decode workspace NULL or smaller than required */
-  ATTN_ERR_HIP = 7          /* the HIP runtime refused the launch */
+  ATTN_ERR_HIP = 7,         /* the HIP runtime refused the launch */
+  ATTN_ERR_SCRATCH = 8      /* attn_decode_noalloc: the sizes need more workspace than
+                               its static scratch (ATTN_DECODE_NOALLOC_SCRATCH_BYTES) */
 } attn_status_t;
+
+/* Size of the static device array attn_decode_noalloc uses as its workspace
+ * (32 MiB per device): enough for attn_decode_workspace_bytes of (for example
+ * B = 64, Hq = 32, d = 128 up to Lmax = 15360). */
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /* Prefill: every query row attends to the keys of its (batch, kv head). */
 typedef struct {
@@ -284,6 +291,25 @@ size_t attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Lmax, int64_t 
  */
 attn_status_t attn_decode(const attn_decode_args_t *args, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/*
+ * attn_decode_noalloc - attn_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same two kernels and results, with the workspace
+ * in a static device array of ATTN_DECODE_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every device it runs on, from the first call on that
+ * device until the process ends.  The call allocates nothing (no hipMalloc,
+ * no allocating library routine); the first call on a device looks up the
+ * array's device address (hipGetSymbolAddress) and keeps it.  The caller
+ * still owns and passes every input and output.  Sizes whose
+ * attn_decode_workspace_bytes exceed the array return ATTN_ERR_SCRATCH
+ * before anything is enqueued.  All calls on one device share that device's
+ * array and leave their partial results in it: calls that may overlap on one
+ * device (different streams, different threads without ordering) race and
+ * must be ordered by the caller, e.g. on one stream.  Errors as attn_decode;
+ * ATTN_ERR_HIP if the array's address cannot be obtained.
+ */
+attn_status_t attn_decode_noalloc(const attn_decode_args_t *args, void *stream);
 
 /*
  * attn_bwd_workspace_bytes - bytes of device workspace attn_bwd needs (two

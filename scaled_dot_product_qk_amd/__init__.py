@@ -19,9 +19,10 @@ LIB_PATH = os.path.join(HERE, "libattn_gfx950.so")
 ATTN_BF16, ATTN_F32 = 0, 1
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_DTYPE",
                 4: "ATTN_ERR_LAYOUT", 5: "ATTN_ERR_UNSUPPORTED", 6: "ATTN_ERR_WORKSPACE",
-                7: "ATTN_ERR_HIP"}
+                7: "ATTN_ERR_HIP", 8: "ATTN_ERR_SCRATCH"}
+ATTN_DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20  # static workspace of attn_decode_noalloc, per device
 EXPORTED = ("attn_fwd", "attn_fwd_masked", "attn_fwd_varlen", "attn_fwd_fp8", "attn_bwd",
-            "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_workspace_bytes",
+            "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_noalloc", "attn_decode_workspace_bytes",
             "attn_validate_fwd",
             "attn_validate_fwd_masked", "attn_validate_fwd_varlen", "attn_validate_fwd_fp8",
             "attn_validate_bwd", "attn_validate_decode", "attn_status_str", "attn_kernel_name",
@@ -132,6 +133,8 @@ def lib() -> ctypes.CDLL:
         L.attn_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p, ctypes.c_size_t,
                                   ctypes.c_void_p]
         L.attn_decode.restype = ctypes.c_int
+        L.attn_decode_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
+        L.attn_decode_noalloc.restype = ctypes.c_int
         L.attn_validate_decode.argtypes = [ctypes.POINTER(DecodeArgs)]
         L.attn_validate_decode.restype = ctypes.c_int
         L.attn_decode_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
@@ -486,6 +489,34 @@ def attn_decode(q, k_cache, v_cache, seqlens, scale: Optional[float] = None, wor
                            _stream_handle(stream))
     if st != 0:
         raise AttnError(st, "attn_decode")
+    return out, lse
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, seqlens, out, lse, scale: Optional[float] = None, stream=None):
+    """attn_decode with the library's static device workspace: the C entry
+    point allocates nothing, and neither does this call, so the caller passes
+    the outputs out [B,Hq,d] and lse [B,Hq] (float32, contiguous).  Calls that
+    may overlap on one device share that workspace and must be ordered (one
+    stream).  Sizes needing more than ATTN_DECODE_NOALLOC_SCRATCH_BYTES of
+    workspace raise AttnError (ATTN_ERR_SCRATCH)."""
+    import torch
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [B,Hq,d] and the caches [B,Hkv,Lmax,d]")
+    if seqlens.dtype != torch.int32 or seqlens.numel() != q.shape[0]:
+        raise ValueError("seqlens must be int32 [B]")
+    for t in (q, k_cache, v_cache):
+        if t.numel() and t.stride(-1) != 1:
+            raise ValueError("head_dim must be the innermost, contiguous dimension")
+    _check_device(q, k_cache, v_cache, seqlens, out, lse)
+    B, Hq, _ = q.shape
+    if not lse.is_contiguous() or lse.dtype != torch.float32 or lse.shape != (B, Hq):
+        raise ValueError("lse must be a contiguous float32 [B, Hq] tensor")
+    if out.shape != q.shape or out.dtype != q.dtype or (out.numel() and out.stride(-1) != 1):
+        raise ValueError("out must match q's shape and dtype with a contiguous head_dim")
+    args = make_decode_args(q, k_cache, v_cache, seqlens, out, lse, scale)
+    st = lib().attn_decode_noalloc(ctypes.byref(args), _stream_handle(stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode_noalloc")
     return out, lse
 
 

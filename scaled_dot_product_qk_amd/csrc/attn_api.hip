@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <limits>
+#include <mutex>
 
 #include "attn.h"
 #include "bwd_bf16.h"
@@ -572,16 +573,10 @@ static attn_status_t launch_decode(const DecodeParams& p, int B, hipStream_t s) 
   return launch_status();
 }
 
-extern "C" attn_status_t attn_decode(const attn_decode_args_t* a, void* workspace, size_t workspace_bytes,
-                          void* stream) {
-  const attn_status_t st = attn_validate_decode(a);
-  if (st != ATTN_OK) return st;
-  if (a->B == 0 || a->Hq == 0) return ATTN_OK;
-  const size_t need = attn_decode_workspace_bytes(a->B, a->Hq, a->Lmax, a->d);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
-  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_LAYOUT;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-
+// Enqueues the decode kernels for validated arguments, with the partial
+// results in `workspace` (attn_decode_workspace_bytes bytes, 256-byte
+// aligned).
+static attn_status_t decode_enqueue(const attn_decode_args_t* a, void* workspace, hipStream_t s) {
   DecodeParams p;
   p.q = a->q; p.k = a->k_cache; p.v = a->v_cache; p.seqlens = a->seqlens;
   const int64_t rows = a->B * a->Hq * decode_pieces(a->Lmax);
@@ -615,6 +610,55 @@ extern "C" attn_status_t attn_decode(const attn_decode_args_t* a, void* workspac
   return ATTN_ERR_UNSUPPORTED;
 }
 
+extern "C" attn_status_t attn_decode(const attn_decode_args_t* a, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  const attn_status_t st = attn_validate_decode(a);
+  if (st != ATTN_OK) return st;
+  if (a->B == 0 || a->Hq == 0) return ATTN_OK;
+  const size_t need = attn_decode_workspace_bytes(a->B, a->Hq, a->Lmax, a->d);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_LAYOUT;
+  return decode_enqueue(a, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+// ---- attn_decode_noalloc: the decode workspace in a static device array ----
+// Every device the library runs on holds its own copy of `scratch` from the
+// first launch on it until the process ends.  In host code the array's name
+// is only a host-side stand-in, so the device address of each device's copy
+// is looked up once per device (with that device current) and kept.
+static __device__ __align__(256) unsigned char scratch[ATTN_DECODE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices] = {nullptr};
+
+// Device address of the current device's scratch array, or nullptr if the
+// runtime cannot give it.
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    scratch_ptr[dev] = ptr;
+  }
+  return scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" attn_status_t attn_decode_noalloc(const attn_decode_args_t* a, void* stream) {
+  const attn_status_t st = attn_validate_decode(a);
+  if (st != ATTN_OK) return st;
+  if (a->B == 0 || a->Hq == 0) return ATTN_OK;
+  const size_t need = attn_decode_workspace_bytes(a->B, a->Hq, a->Lmax, a->d);
+  if (need > (size_t)ATTN_DECODE_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_SCRATCH;
+  void* ws = device_scratch();
+  if (ws == nullptr) return ATTN_ERR_HIP;
+  return decode_enqueue(a, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
 extern "C" const char* attn_status_str(attn_status_t s) {
   switch (s) {
     case ATTN_OK: return "ok";
@@ -625,6 +669,7 @@ extern "C" const char* attn_status_str(attn_status_t s) {
     case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
     case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case ATTN_ERR_HIP: return "HIP launch error";
+    case ATTN_ERR_SCRATCH: return "sizes need more than the static decode scratch (attn_decode_noalloc)";
   }
   return "unknown status";
 }

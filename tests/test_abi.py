@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for s in range(8):
+    for s in range(9):
         assert sdpa.status_str(s) and sdpa.status_str(s) != "unknown status"
     assert sdpa.status_str(99) == "unknown status"
 
@@ -416,3 +416,27 @@ def test_fp8_empty_inputs_are_valid_noops():
         assert sdpa.lib().attn_fwd_fp8(ctypes.byref(a), None) == OK
     assert vfp8(Lk=0, k=0, v=0) == OK
     assert sdpa.lib().attn_validate_fwd_fp8(None) == NULL
+
+
+# ------------------------------------------------------- attn_decode_noalloc
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), NULL), (dict(dtype=1), UNSUP), (dict(d=80), UNSUP), (dict(Hkv=3), SHAPE),
+    (dict(q=P + 2), LAYOUT), (dict(B=64, Lmax=40_000_000), UNSUP),
+])
+def test_decode_noalloc_rejections(kw, status):
+    """Argument errors come back before the library touches the device."""
+    assert sdpa.lib().attn_decode_noalloc(ctypes.byref(dec_args(**kw)), None) == status
+
+
+def test_decode_noalloc_scratch_limit():
+    """Sizes whose workspace exceeds the static scratch are refused with
+    ATTN_ERR_SCRATCH, before any device work; the largest decode cache that
+    fits at B=64, Hq=32, d=128 is Lmax=15360 (31 pieces per sequence)."""
+    L = sdpa.lib()
+    lim = sdpa.ATTN_DECODE_NOALLOC_SCRATCH_BYTES
+    assert sdpa.attn_decode_workspace_bytes(64, 32, 15360, 128) <= lim
+    assert sdpa.attn_decode_workspace_bytes(64, 32, 15361, 128) > lim
+    big = dec_args(B=64, Hq=32, Hkv=8, Lmax=15361, d=128)
+    assert L.attn_decode_noalloc(ctypes.byref(big), None) == 8
+    assert sdpa.status_str(8) != "unknown status"
+    assert L.attn_decode_noalloc(ctypes.byref(dec_args(B=0)), None) == OK
