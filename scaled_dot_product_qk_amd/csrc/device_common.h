@@ -101,6 +101,11 @@ __device__ __forceinline__ void lds_copy4(const void* base, uint32_t off, uint32
   asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_base) : "memory");
 }
 
+// s_waitcnt immediate that waits until at most n vector memory operations
+// are outstanding (vmcnt(n), n < 64: bits 3:0 and 15:14) and leaves the
+// other counters unconstrained (expcnt 7, lgkmcnt 15).
+__host__ __device__ constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
+
 // Marks the end of one group of copies in the assembly (an assembler
 // comment; no instruction).  A kernel that waits with vmcnt(N) for all but
 // its last group of N copies relies on every group issuing exactly N copy

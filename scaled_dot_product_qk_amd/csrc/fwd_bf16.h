@@ -76,10 +76,10 @@ struct FwdParams {
 
 // Work-item order shared by the prefill kernels.  The hardware hands
 // consecutive workgroup ids to the 8 XCDs in turn; this maps them so that each
-// XCD receives one contiguous range of work items, and orders work items kv
-// head by kv head, so the workgroups that re-read one head's K and V run on
-// the same XCD and share its L2.  Within a kv head: query tiles (heaviest
-// first when causal), then the query heads of the group.
+// XCD receives whole (batch, kv head) units, so the workgroups that re-read
+// one head's K and V run on the same XCD and share its L2.  Not causal:
+// unit by unit, then query tiles, then the query heads of the group.  Causal:
+// query tiles heaviest first across the XCD's units (see below).
 struct WorkItem {
   int b, h, hk, qt;
 };
@@ -123,6 +123,28 @@ __device__ __forceinline__ WorkItem prefill_work_item(const FwdParams& p, bool c
     const int qi = r / nb;
     it.h = it.hk * p.group + hg;
     it.qt = causal ? p.n_qtiles - 1 - qi : qi;
+    return it;
+  }
+  // Causal, with the (batch, kv head) units splitting evenly over the 8
+  // XCDs: XCD x serves units x U/8 .. (x+1) U/8 - 1, and on it the items go
+  // query tile by query tile, heaviest first, across all of its units (the
+  // group's query heads fastest).  Unit by unit, each unit's tiles heaviest
+  // first, would leave the heavy tiles of the XCD's last units to run alone
+  // at the end when an XCD holds many units of few tiles (at B=4, H=16,
+  // n=2048: 8 units of 16 tiles, two thirds of the XCD busy on average).
+  const int units = N / (p.n_qtiles * p.group);
+  if (causal && (units & 7) == 0) {
+    const int upx = units >> 3;  // units per XCD
+    const int i = L >> 3;
+    WorkItem it;
+    const int hg = i % p.group;
+    const int r = i / p.group;
+    const int unit = (L & 7) * upx + r % upx;
+    const int qi = r / upx;
+    it.hk = unit % p.Hkv;
+    it.b = unit / p.Hkv;
+    it.h = it.hk * p.group + hg;
+    it.qt = p.n_qtiles - 1 - qi;
     return it;
   }
   const int full = N & ~7;
@@ -178,7 +200,7 @@ struct Bf16FwdShape {
 // otherwise.  (The causal instance would need more than 256 registers per
 // lane for the pipeline: its diagonal tiles' masking spills Q's operands.)
 __host__ __device__ constexpr int bf16_fwd_kv_stages(int d, bool causal, int mk) {
-  return d == 64 && !causal && mk == 0 ? 3 : 2;
+  return d == 64 && mk == 0 ? 3 : 2;
 }
 
 // Attention-mask tiles (MK: 1 uint8 boolean, 2 bf16 additive): the
@@ -637,8 +659,12 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
   // group closed by a scheduling barrier.  Left to the scheduler, the
   // products of a phase bunched together and the vector work ran alone after
   // them.  The arithmetic and its order are those of exp_half.
-  auto fused_half = [&](int sb, const u32x4 (&va)[S::kND][2], const u32x4 (&ka)[S::kKC])
+  // MASK: the tile holds keys beyond Lk or (causal) after some query of the
+  // wave; those scores are set to -inf as their probabilities are formed
+  // (and left so in s, for the exact path).
+  auto fused_half = [&](auto mask_tag, int kv0, int sb, const u32x4 (&va)[S::kND][2], const u32x4 (&ka)[S::kKC])
                         __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     if constexpr (kPipe) {
       static_assert(NB == 2 && S::kND == 2 && S::kKC == 4, "one product per two probabilities");
       const int ob = 1 - sb;
@@ -658,6 +684,15 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
           s[nb][ob] = mfma32(ka[kc], qop[nb][kc], s[nb][ob]);
         }
         const int nb = k >> 3, w = k & 7;  // probabilities 2w, 2w + 1 of row block nb
+        if constexpr (MASK) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int r = 2 * w + e;
+            const int key = kv0 + 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3);
+            const bool vis = key < p.Lk && (!CAUSAL || key <= qrow[nb]);
+            s[nb][sb][r] = vis ? s[nb][sb][r] : kNegInf;
+          }
+        }
         const float e0 = fast_exp2(__builtin_fmaf(s[nb][sb][2 * w], c, -m_run[nb]));
         const float e1 = fast_exp2(__builtin_fmaf(s[nb][sb][2 * w + 1], c, -m_run[nb]));
         if (w < 2) {
@@ -696,12 +731,12 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
   if (n_tiles > 0) issue_tile(0, 0);
   if (n_tiles > 1) {
     issue_tile(1, 1);
-    __builtin_amdgcn_s_waitcnt(0x0f70 | (S::kCopiesPerWave + MS::kCopiesPerWave));  // vmcnt: tile 0's copies done
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::kCopiesPerWave + MS::kCopiesPerWave));  // tile 0's copies done
   } else {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   }
   __syncthreads();
-  auto active = [&](int t) { return t < n_tiles && (!CAUSAL || t * S::kBC <= wave_last_row); };
+  auto active = [&](int t) { return t < n_tiles && (kPipe || !CAUSAL || t * S::kBC <= wave_last_row); };
   if (active(0)) read_k(0, 0, ka_next);
 
   // Between the halves of tile t: wait for this wave's copies of tile t + 1
@@ -753,26 +788,14 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
     // only at the barrier of tile t + 1).
     auto phase_a = [&](auto mask_tag, int t, int buf) __attribute__((always_inline)) {
       read_k(buf, 1, ka1);
-      if constexpr (!decltype(mask_tag)::value) {
-        fused_half(0, va_last, ka1);
-      } else {
-        pv(1, va_last);
-        qk(1, ka1);
-        softmax_half(mask_tag, buf, t * S::kBC, 0, BothTag{});
-      }
+      fused_half(mask_tag, t * S::kBC, 0, va_last, ka1);
       read_v(buf, 0, va0);
     };
     // Phase B; the products S(t + 1, 0) are issued whether or not the wave
     // is active in tile t + 1 (then on stale operands, and never used), so
     // that they stay in one scheduling region with the softmax.
     auto phase_b = [&](auto mask_tag, int t, int buf) __attribute__((always_inline)) {
-      if constexpr (!decltype(mask_tag)::value) {
-        fused_half(1, va0, ka_next);
-      } else {
-        pv(0, va0);
-        qk(0, ka_next);
-        softmax_half(mask_tag, buf, t * S::kBC, 1, BothTag{});
-      }
+      fused_half(mask_tag, t * S::kBC, 1, va0, ka_next);
       read_v(buf, 1, va_last);
       if (!active(t + 1)) pv(1, va_last);  // the wave's last tile
     };
