@@ -404,24 +404,16 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, ln = lane & 31;
-  // Work order as in the forward: each XCD receives one contiguous range of
-  // work items ordered (batch, kv head, query block, query head of the
-  // group), heaviest query blocks first when causal, so the workgroups that
-  // re-read one kv head's K and V share an L2.
+  // Work order as in the forward (whole (batch, kv head) units per XCD, so
+  // the workgroups that re-read one kv head's K and V share an L2; causal:
+  // heaviest query blocks first across the XCD's units).
   const int n_qb = (p.Lq + 127) / 128;
   int h, b, qb;
   {
-    const int L = blockIdx.x, N = gridDim.x;
-    const int full = N & ~7;
-    const int w = L < full ? (L & 7) * (full >> 3) + (L >> 3) : L;
-    const int hg = w % p.group;
-    int r = w / p.group;
-    const int qi = r % n_qb;
-    r /= n_qb;
-    const int hk = r % p.Hkv;
-    b = r / p.Hkv;
-    h = hk * p.group + hg;
-    qb = CAUSAL ? n_qb - 1 - qi : qi;
+    const WorkItem it = dense_work_item(blockIdx.x, gridDim.x, n_qb, p.group, p.Hkv, CAUSAL);
+    h = it.h;
+    b = it.b;
+    qb = it.qt;
   }
   const int hk = h / p.group;
   const int q0 = qb * 128;

@@ -113,6 +113,52 @@ __host__ __device__ constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | 
 // of the compiled code count them per group.
 __device__ __forceinline__ void copy_group_end() { asm volatile(";;#copy-group-end"); }
 
+// A work item of the prefill-shaped kernels (forward, backward dQ).
+struct WorkItem {
+  int b, h, hk, qt;
+};
+
+// Dense layout: workgroup L of N over work items (batch, query head, query
+// tile) with n_qtiles tiles per head, Hkv kv heads and `group` query heads
+// per kv head.
+__device__ __forceinline__ WorkItem dense_work_item(int L, int N, int n_qtiles, int group, int Hkv, bool causal) {
+  // Causal, with the (batch, kv head) units splitting evenly over the 8
+  // XCDs: XCD x serves units x U/8 .. (x+1) U/8 - 1, and on it the items go
+  // query tile by query tile, heaviest first, across all of its units (the
+  // group's query heads fastest).  Unit by unit, each unit's tiles heaviest
+  // first, would leave the heavy tiles of the XCD's last units to run alone
+  // at the end when an XCD holds many units of few tiles (at B=4, H=16,
+  // n=2048: 8 units of 16 tiles, two thirds of the XCD busy on average).
+  const int units = N / (n_qtiles * group);
+  if (causal && (units & 7) == 0) {
+    const int upx = units >> 3;  // units per XCD
+    const int i = L >> 3;
+    WorkItem it;
+    const int hg = i % group;
+    const int r = i / group;
+    const int unit = (L & 7) * upx + r % upx;
+    const int qi = r / upx;
+    it.hk = unit % Hkv;
+    it.b = unit / Hkv;
+    it.h = it.hk * group + hg;
+    it.qt = n_qtiles - 1 - qi;
+    return it;
+  }
+  const int full = N & ~7;
+  int w = L;
+  if (L < full) w = (L & 7) * (full >> 3) + (L >> 3);
+  WorkItem it;
+  const int hg = w % group;
+  int r = w / group;
+  const int qi = r % n_qtiles;
+  r /= n_qtiles;
+  it.hk = r % Hkv;
+  it.b = r / Hkv;
+  it.h = it.hk * group + hg;
+  it.qt = causal ? n_qtiles - 1 - qi : qi;
+  return it;
+}
+
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

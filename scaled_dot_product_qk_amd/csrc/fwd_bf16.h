@@ -80,9 +80,7 @@ struct FwdParams {
 // one head's K and V run on the same XCD and share its L2.  Not causal:
 // unit by unit, then query tiles, then the query heads of the group.  Causal:
 // query tiles heaviest first across the XCD's units (see below).
-struct WorkItem {
-  int b, h, hk, qt;
-};
+
 
 //
 // Packed sequences of different lengths make the work per item uneven across
@@ -125,41 +123,7 @@ __device__ __forceinline__ WorkItem prefill_work_item(const FwdParams& p, bool c
     it.qt = causal ? p.n_qtiles - 1 - qi : qi;
     return it;
   }
-  // Causal, with the (batch, kv head) units splitting evenly over the 8
-  // XCDs: XCD x serves units x U/8 .. (x+1) U/8 - 1, and on it the items go
-  // query tile by query tile, heaviest first, across all of its units (the
-  // group's query heads fastest).  Unit by unit, each unit's tiles heaviest
-  // first, would leave the heavy tiles of the XCD's last units to run alone
-  // at the end when an XCD holds many units of few tiles (at B=4, H=16,
-  // n=2048: 8 units of 16 tiles, two thirds of the XCD busy on average).
-  const int units = N / (p.n_qtiles * p.group);
-  if (causal && (units & 7) == 0) {
-    const int upx = units >> 3;  // units per XCD
-    const int i = L >> 3;
-    WorkItem it;
-    const int hg = i % p.group;
-    const int r = i / p.group;
-    const int unit = (L & 7) * upx + r % upx;
-    const int qi = r / upx;
-    it.hk = unit % p.Hkv;
-    it.b = unit / p.Hkv;
-    it.h = it.hk * p.group + hg;
-    it.qt = p.n_qtiles - 1 - qi;
-    return it;
-  }
-  const int full = N & ~7;
-  int w = L;
-  if (L < full) w = (L & 7) * (full >> 3) + (L >> 3);
-  WorkItem it;
-  const int hg = w % p.group;
-  int r = w / p.group;
-  const int qi = r % p.n_qtiles;
-  r /= p.n_qtiles;
-  it.hk = r % p.Hkv;
-  it.b = r / p.Hkv;
-  it.h = it.hk * p.group + hg;
-  it.qt = causal ? p.n_qtiles - 1 - qi : qi;
-  return it;
+  return dense_work_item(L, N, p.n_qtiles, p.group, p.Hkv, causal);
 }
 
 // 32-query column blocks per wave: two at head_dim 64 (each K or V^T read
@@ -525,6 +489,20 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) s[nb][sb] = mfma32(ka[kc], qop[nb][kc], s[nb][sb]);
   };
+  // Both halves' scores, the two accumulation chains interleaved.
+  auto qk_both = [&](const u32x4 (&k0)[S::kKC], const u32x4 (&k1)[S::kKC]) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[nb][0][r] = s[nb][1][r] = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < S::kKC; ++kc)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        s[nb][0] = mfma32(k0[kc], qop[nb][kc], s[nb][0]);
+        s[nb][1] = mfma32(k1[kc], qop[nb][kc], s[nb][1]);
+      }
+  };
   // (the 16-key slices j outermost, so that consecutive products accumulate
   // into different output blocks even with one row block per wave)
   auto pv = [&](int sb, const u32x4 (&va)[S::kND][2]) {
@@ -644,10 +622,12 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
       redo = redo || !(ls[nb] <= kSumGuard) || (MK != 0 && m_run[nb] == kNegInf);
     }
     // about 60 vector instructions per row block: one product per share
+    if constexpr (N_MFMA > 0) {
 #pragma unroll
-    for (int i = 0; i < N_MFMA; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 56 * NB / N_MFMA, 0);
+      for (int i = 0; i < N_MFMA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 56 * NB / N_MFMA, 0);
+      }
     }
     finish_half(sb, redo, ls);
   };
@@ -724,6 +704,7 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
   using QKTag = std::integral_constant<int, kQKMfma>;
   using PVTag = std::integral_constant<int, kPVMfma>;
   using BothTag = std::integral_constant<int, kQKMfma + kPVMfma>;
+  using NoneTag = std::integral_constant<int, 0>;
 
   // Q must have landed before the first copy: the copies are invisible to the
   // compiler, and a later wait for Q would not know to let them run on.
@@ -828,12 +809,23 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
       const int buf = t & 1, kv0 = t * S::kBC;
       if (act) {
         read_k(buf, 1, ka1);
-        __builtin_amdgcn_s_setprio(2);
-        qk(0, ka_next);
-        __builtin_amdgcn_s_setprio(0);
-        read_v(buf, 0, va0);
-        qk(1, ka1);
-        softmax_half(mask_tag, buf, kv0, 0, QKTag{});
+        if constexpr (NB == 1) {
+          // One row block per wave: both halves' scores first, their two
+          // accumulation chains interleaved; the softmax of the first half
+          // then runs beside the other wave's products.  (Same speed as
+          // the first half's scores alone before it, and no spilled
+          // registers at head_dim 128, where that order spilled 9.)
+          qk_both(ka_next, ka1);
+          read_v(buf, 0, va0);
+          softmax_half(mask_tag, buf, kv0, 0, NoneTag{});
+        } else {
+          __builtin_amdgcn_s_setprio(2);
+          qk(0, ka_next);
+          __builtin_amdgcn_s_setprio(0);
+          read_v(buf, 0, va0);
+          qk(1, ka1);
+          softmax_half(mask_tag, buf, kv0, 0, QKTag{});
+        }
         read_v(buf, 1, va_last);
         pv(0, va0);
         softmax_half(mask_tag, buf, kv0, 1, PVTag{});
