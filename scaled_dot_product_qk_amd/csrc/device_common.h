@@ -121,7 +121,11 @@ struct WorkItem {
 // Dense layout: workgroup L of N over work items (batch, query head, query
 // tile) with n_qtiles tiles per head, Hkv kv heads and `group` query heads
 // per kv head.
-__device__ __forceinline__ WorkItem dense_work_item(int L, int N, int n_qtiles, int group, int Hkv, bool causal) {
+//
+// tile_major: the causal order below (also taken for a mask shared by all
+// heads).
+__device__ __forceinline__ WorkItem dense_work_item(int L, int N, int n_qtiles, int group, int Hkv, bool tile_major) {
+  const bool causal = tile_major;
   // Causal, with the (batch, kv head) units splitting evenly over the 8
   // XCDs: XCD x serves units x U/8 .. (x+1) U/8 - 1, and on it the items go
   // query tile by query tile, heaviest first, across all of its units (the

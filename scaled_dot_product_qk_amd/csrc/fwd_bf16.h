@@ -123,7 +123,11 @@ __device__ __forceinline__ WorkItem prefill_work_item(const FwdParams& p, bool c
     it.qt = causal ? p.n_qtiles - 1 - qi : qi;
     return it;
   }
-  return dense_work_item(L, N, p.n_qtiles, p.group, p.Hkv, causal);
+  // A mask shared by every head (head stride 0) gets the causal order too:
+  // the heads of an XCD then read a query tile's mask rows at about the same
+  // time.
+  const bool shared_mask = p.mask != nullptr && p.m_sh == 0;
+  return dense_work_item(L, N, p.n_qtiles, p.group, p.Hkv, causal || shared_mask);
 }
 
 // 32-query column blocks per wave: two at head_dim 64 (each K or V^T read
