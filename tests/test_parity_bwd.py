@@ -3,13 +3,18 @@
 The GPU forward supplies O and LSE exactly as a caller's would; the oracle's
 gradients come from the bf16 input values widened to float64.  Small and
 medium shapes are compared in full; the causal GQA n=8192 d=128 workload at
-its real size on sampled query rows and keys.  Gate per gradient tensor: the
-stated bf16 tolerance (max-abs <= 2e-2, mean-abs <= 1e-3) applied to the
-tensor divided by s = max(1, max |reference|).  Gradients, unlike O, are not
-bounded by the values' range (a kv head's dV sums the output gradients of its
-query rows and heads), and rounding a result to bf16 alone moves it by up to
-2^-9 of its magnitude; dividing by s keeps the stated bound wherever values
-stay within +-1 and makes it relative where they are larger.
+its real size on sampled query rows and keys.
+
+Gate, element by element: |got - ref| <= 2e-2 + 2^-8 |ref|, and per tensor
+mean |got - ref| <= 1e-3 + 2^-9 mean |ref|.  The constant terms are the
+stated bf16 tolerance.  The other terms are the rounding of the result to
+bf16, which the gradients cannot avoid: unlike O they are not bounded by the
+values' range (a kv head's dV sums the output gradients of all its query rows
+and heads, |dV| reaches 10-13 here), and round-to-nearest-even to bf16 moves
+a value x by at most half an ulp, <= 2^-8 |x|, by ulp/4 <= 2^-9 |x| on
+average.  So an element of magnitude below ~1 is held to the stated 2e-2,
+and only the part of the error that output rounding explains is added above
+that.
 """
 import numpy as np
 import pytest
@@ -29,16 +34,23 @@ def dev():
     return torch.device("cuda:0")
 
 
+ROUND_MAX = 2.0 ** -8   # half an ulp of bf16, relative
+ROUND_MEAN = 2.0 ** -9  # mean rounding error of bf16 (ulp / 4), relative
+
+
 def grad_check(name, got, ref, label):
     got = np.asarray(got, np.float64)
     d = np.abs(got - ref)
+    a = np.abs(ref)
+    gate = BF16_MAX_ABS + ROUND_MAX * a
     e = dict(max_abs=float(d.max()) if d.size else 0.0, mean_abs=float(d.mean()) if d.size else 0.0,
-             ref_max=float(np.abs(ref).max()) if ref.size else 0.0)
+             ref_max=float(a.max()) if a.size else 0.0,
+             worst_over_gate=float((d / gate).max()) if d.size else 0.0,
+             mean_over_gate=float(d.mean() / (BF16_MEAN_ABS + ROUND_MEAN * a.mean())) if d.size else 0.0)
     print(f"[parity] {label} {name}: " + " ".join(f"{k}={v:.3e}" for k, v in e.items()), flush=True)
     assert np.isfinite(got).all(), f"non-finite values in {name}"
-    sc = max(1.0, e["ref_max"])
-    assert e["max_abs"] <= BF16_MAX_ABS * sc, (name, e)
-    assert e["mean_abs"] <= BF16_MEAN_ABS * sc, (name, e)
+    assert e["worst_over_gate"] <= 1.0, (name, e)
+    assert e["mean_over_gate"] <= 1.0, (name, e)
 
 
 def inputs(w, seed_do):
