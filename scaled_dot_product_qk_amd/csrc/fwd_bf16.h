@@ -189,6 +189,20 @@ struct FwdMaskShape {
   static constexpr int kCopiesPerWave = kCopies / S::kWaves;
   static constexpr int kLdsBytes = MK == 0 ? 0 : 2 * kTileBytes;
   static_assert(MK == 0 || kCopies % S::kWaves == 0, "mask copies split evenly over the waves");
+  // A mask row's 16-byte chunks are XOR-swizzled by the row index: chunk c
+  // of row r sits in slot c ^ swz(r), swz(r) = (r / kRowsPerSpan) %
+  // kChunksPerRow, kRowsPerSpan being the rows in one pass over the 64 banks
+  // (256 bytes).  A mask read takes the same key offset from 32 rows; without
+  // the swizzle those fall on 4 (boolean) or 2 (additive) bank positions,
+  // with it on 16, so the read is 2-way instead of 8- or 16-way conflicted.
+  static constexpr int kRowsPerSpan = 256 / kRowBytes;
+  static constexpr int kSwzRows = kRowsPerSpan * kChunksPerRow;  // period of swz
+  static constexpr int kSwzVar = kSwzRows > kRowsPerCopy ? kSwzRows / kRowsPerCopy : 1;
+  static_assert(MK == 0 || (kCopiesPerWave * kRowsPerCopy) % kSwzRows == 0,
+                "each wave's first mask row starts a swizzle period");
+  static_assert(MK == 0 || (S::kRowsPerWave % kSwzRows == 0 && 32 % kSwzRows == 0),
+                "a query row's swizzle depends on its lane only");
+  __device__ static int swz(int r) { return (r / kRowsPerSpan) % kChunksPerRow; }
   // dynamic LDS of the kernel: key/value buffers, then the mask tiles
   static constexpr int kKVBytes = bf16_fwd_kv_stages(D, CAUSAL, MK) * S::kBufBytes;
   static constexpr int kKernelLdsBytes = kKVBytes + kLdsBytes;
@@ -342,15 +356,18 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
   // 16-byte chunk l % chunks-per-row.
   const char* m_base = nullptr;
   int64_t m_row_bytes = 0;
-  int m_lrow = 0, m_chunk = 0, m_row0 = 0;
+  int m_lrow = 0, m_row0 = 0;
+  int m_key[MS::kSwzVar];  // first key, within the tile, of the chunk the lane fetches
   uint32_t m_lds0 = 0;
   if constexpr (MK != 0) {
     m_base = reinterpret_cast<const char*>(p.mask) + (b * p.m_sb + h * p.m_sh) * MS::kEs;
     m_row_bytes = p.m_sq * MS::kEs;
     m_lrow = lane / MS::kChunksPerRow;
-    m_chunk = lane % MS::kChunksPerRow;
     m_row0 = wave * MS::kCopiesPerWave * MS::kRowsPerCopy;
     m_lds0 = (uint32_t)(uintptr_t)lds_b + MS::kKVBytes;
+#pragma unroll
+    for (int v = 0; v < MS::kSwzVar; ++v)
+      m_key[v] = MS::kChunkKeys * ((lane % MS::kChunksPerRow) ^ MS::swz(MS::kRowsPerCopy * v + m_lrow));
   }
   // Full tiles copy without checks; the tile holding key Lk - 1 reads rows
   // beyond it from row Lk - 1 instead (in bounds and finite), and those keys
@@ -378,11 +395,12 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
       // Mask rows q0 + m_row0 + ... of this tile's 64 keys.  Every lane
       // copies (rows past Lq repeat row Lq - 1, chunks past Lk repeat the
       // last chunk; both are masked anyway), so each wave issues exactly
-      // MS::kCopiesPerWave copies per tile.
+      // MS::kCopiesPerWave copies per tile.  Lane l fills slot l % chunks-
+      // per-row of its row and fetches the chunk the swizzle puts there.
       const uint32_t mdst = m_lds0 + (t & 1) * MS::kTileBytes;
-      const int kc0 = min(kv0 + m_chunk * MS::kChunkKeys, p.Lk - MS::kChunkKeys);
 #pragma unroll
       for (int j = 0; j < MS::kCopiesPerWave; ++j) {
+        const int kc0 = min(kv0 + m_key[j % MS::kSwzVar], p.Lk - MS::kChunkKeys);
         const int r = q0 + m_row0 + MS::kRowsPerCopy * j;
         const int ra = min(r, p.Lq - 1), rl = min(r + m_lrow, p.Lq - 1);
         fwd_copy16(m_base + (int64_t)ra * m_row_bytes, (uint32_t)(rl - ra) * (uint32_t)m_row_bytes + kc0 * MS::kEs,
@@ -595,13 +613,15 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
       // Keys 32 sb + 8 j + 4 g + 0..3 of this lane's query row in the mask
       // tile: a boolean removes pairs, an additive mask enters the raw score
       // as mask / |scale| (so the exponent gets scale s + mask, in log2 units).
+      // Query row 32 nb + lq of the wave has swizzle swz(lq).
       const lds_char* mt = lds_b + MS::kKVBytes + buf * MS::kTileBytes;
+      const int m_x = 16 * MS::swz(lq);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const lds_char* mrow = mt + (wave * S::kRowsPerWave + 32 * nb + lq) * MS::kRowBytes;
+        const lds_char* mrow = mt + (wave * S::kRowsPerWave + 32 * nb + lq) * MS::kRowBytes + 4 * g * MS::kEs;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int off = (32 * sb + 8 * j + 4 * g) * MS::kEs;
+          const int off = ((32 * sb + 8 * j) * MS::kEs) ^ m_x;  // flips bits 4 and up only
           if constexpr (MK == 1) {
             const uint32_t w = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(mrow + off);
 #pragma unroll
