@@ -80,8 +80,6 @@ struct FwdParams {
 // one head's K and V run on the same XCD and share its L2.  Not causal:
 // unit by unit, then query tiles, then the query heads of the group.  Causal:
 // query tiles heaviest first across the XCD's units (see below).
-
-
 //
 // Packed sequences of different lengths make the work per item uneven across
 // sequences, so contiguous ranges would load the XCDs unevenly; there the
