@@ -282,7 +282,7 @@ size_t attn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Lmax, int64_t 
  * attn_decode_workspace_bytes(B, Hq, Lmax, d) bytes, 256-byte aligned; its
  * contents on entry do not matter and are overwritten.  Calls that share a
  * workspace must be ordered on one stream.
- * Supported: dtype bf16; d in {64, 128}; Hq % Hkv == 0; B * Lmax < 2^31
+ * Supported: dtype bf16; d in {64, 80, 128}; Hq % Hkv == 0; B * Lmax < 2^31
  * (ATTN_ERR_UNSUPPORTED otherwise).  The query heads of
  * one kv head are served 16 at a time, so a group larger than 16 reads its
  * keys and values once per 16 query heads.  B == 0 or Hq == 0 is a no-op;

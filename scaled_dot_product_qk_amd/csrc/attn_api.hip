@@ -35,7 +35,7 @@ bool strides_ok(const int64_t* s, int n, int elem_bytes) {
 }
 
 bool fwd_head_dim_supported(int64_t d) { return d == 64 || d == 80 || d == 128; }
-bool decode_head_dim_supported(int64_t d) { return d == 64 || d == 128; }
+bool decode_head_dim_supported(int64_t d) { return d == 64 || d == 80 || d == 128; }
 
 int elem_bytes_of(int32_t dtype) { return dtype == ATTN_F32 ? 4 : 2; }
 
@@ -605,6 +605,7 @@ static attn_status_t decode_enqueue(const attn_decode_args_t* a, void* workspace
   p.scale_log2 = effective_scale(a->scale, a->d) * kLog2e;
   switch (a->d) {
     case 64: return launch_decode<64>(p, (int)a->B, s);
+    case 80: return launch_decode<80>(p, (int)a->B, s);
     case 128: return launch_decode<128>(p, (int)a->B, s);
   }
   return ATTN_ERR_UNSUPPORTED;

@@ -138,8 +138,10 @@ __device__ __forceinline__ void dec_find(const DecodeParams& p, int lane, int y,
 
 template <int D>
 __global__ __launch_bounds__(64 * kDecWaves, kDecGroupsPerCU) void attn_decode_split_kernel(DecodeParams p) {
-  static_assert(D % 32 == 0 && D <= 128, "decode head_dim must be 32, 64, 96 or 128");
-  constexpr int KC = D / 32;      // k-slices of S^T = K Q^T
+  static_assert(D % 16 == 0 && D <= 128, "decode head_dim: a multiple of 16, at most 128");
+  // k-slices of S^T = K Q^T, 32 head_dim values each; at head_dim 80 the
+  // last slice's chunks 10 and 11 are zero in both operands (never loaded).
+  constexpr int KC = (D + 31) / 32;
   __shared__ float red_m[kDecWaves][16];
   __shared__ float red_l[kDecWaves][16];
   __shared__ float red_o[kDecWaves][16][D + 1];
@@ -172,7 +174,8 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecGroupsPerCU) void attn_decode_s
     {
       const uint16_t* qr = reinterpret_cast<const uint16_t*>(p.q) + b * p.q_sb + (int64_t)h * p.q_sh;
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) qop[kc] = hvalid ? load16(qr + 8 * (4 * kc + g)) : zero16();
+      for (int kc = 0; kc < KC; ++kc)
+        qop[kc] = hvalid && 8 * (4 * kc + g) < D ? load16(qr + 8 * (4 * kc + g)) : zero16();
     }
 
     const uint16_t* kg = reinterpret_cast<const uint16_t*>(p.k) + b * p.k_sb + hkv * p.k_sh;
@@ -192,7 +195,9 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecGroupsPerCU) void attn_decode_s
       for (int kb = 0; kb < 2; ++kb) {
         const uint16_t* row = kg + (int64_t)min(base + 16 * kb + n, last) * p.k_st;
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) kr[kb][kc] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + 8 * (4 * kc + g)));
+        for (int kc = 0; kc < KC; ++kc)
+          kr[kb][kc] = 8 * (4 * kc + g) < D ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + 8 * (4 * kc + g)))
+                                            : zero16();
       }
     };
     // V rows for the transposed A operand: lane (n, g) loads 8 rows, head_dim
@@ -347,14 +352,16 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecGroupsPerCU) void attn_decode_s
   }
 }
 
-// Merge: one wave per (sequence, query head), D / 64 head_dim values per
-// lane; four (sequence, head) pairs per workgroup.
+// Merge: one wave per (sequence, query head), one head_dim value per lane at
+// head_dim 64, two at 80 and 128 (lanes 40-63 idle at 80); four (sequence,
+// head) pairs per workgroup.
 constexpr int kDecMergeWaves = 4;
 
 template <int D>
 __global__ __launch_bounds__(64 * kDecMergeWaves) void attn_decode_merge_kernel(DecodeParams p) {
-  constexpr int E = D / 64;  // head_dim values per lane
-  static_assert(E * 64 == D, "merge lanes cover head_dim exactly");
+  constexpr int E = (D + 63) / 64;  // head_dim values per lane
+  static_assert(E == 1 ? D == 64 : (E == 2 && D % 2 == 0), "merge lanes cover head_dim 64, or up to 128 in pairs");
+  const bool lane_on = E * (threadIdx.x & 63) < D;  // the lane holds head_dim values
   const int lane = threadIdx.x & 63;
   const int64_t bh = (int64_t)blockIdx.x * kDecMergeWaves + (threadIdx.x >> 6);
   if (bh >= (int64_t)p.B * p.Hq) return;  // whole wave leaves together
@@ -394,7 +401,7 @@ __global__ __launch_bounds__(64 * kDecMergeWaves) void attn_decode_merge_kernel(
       lsv[j] = ok ? p.lse_part[row0 + s0 + j] : kNegInf;
       const float* src = p.o_part + (row0 + s0 + j) * D + E * lane;
       if constexpr (E == 2) {
-        const f32x2 v = ok ? *reinterpret_cast<const f32x2*>(src) : f32x2{0.f, 0.f};
+        const f32x2 v = ok && lane_on ? *reinterpret_cast<const f32x2*>(src) : f32x2{0.f, 0.f};
         ov[j][0] = v[0];
         ov[j][1] = v[1];
       } else {
@@ -420,7 +427,7 @@ __global__ __launch_bounds__(64 * kDecMergeWaves) void attn_decode_merge_kernel(
   uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + b * p.o_sb + (int64_t)h * p.o_sh;
   const float inv = ns > 0 ? 1.f / wsum : 0.f;
   if constexpr (E == 2) {
-    *reinterpret_cast<uint32_t*>(orow + 2 * lane) = pack_bf16x2(acc[0] * inv, acc[1] * inv);  // bf16, RNE
+    if (lane_on) *reinterpret_cast<uint32_t*>(orow + 2 * lane) = pack_bf16x2(acc[0] * inv, acc[1] * inv);  // bf16, RNE
   } else {
     orow[lane] = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.f) & 0xffffu);
   }

@@ -148,7 +148,7 @@ def vdec(**kw):
     return sdpa.lib().attn_validate_decode(ctypes.byref(dec_args(**kw)))
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 80, 128])
 @pytest.mark.parametrize("Hq,Hkv", [(8, 2), (32, 8), (4, 4), (40, 1)])
 def test_decode_valid(d, Hq, Hkv):
     assert vdec(d=d, Hq=Hq, Hkv=Hkv) == OK
@@ -156,7 +156,7 @@ def test_decode_valid(d, Hq, Hkv):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=0), NULL), (dict(seqlens=0), NULL), (dict(k_cache=0), NULL), (dict(lse=0), NULL),
-    (dict(dtype=7), DTYPE), (dict(dtype=1), UNSUP), (dict(d=80), UNSUP), (dict(d=96), UNSUP),
+    (dict(dtype=7), DTYPE), (dict(dtype=1), UNSUP), (dict(d=96), UNSUP), (dict(d=32), UNSUP),
     (dict(Hkv=3), SHAPE), (dict(Hkv=0), SHAPE), (dict(Lmax=-1), SHAPE),
     (dict(scale=float("nan")), SHAPE),
     (dict(q=P + 2), LAYOUT), (dict(seqlens=P + 2), LAYOUT), (dict(ks=(8 * 1000 * 128, 1000 * 128, 130)), LAYOUT),
@@ -420,7 +420,7 @@ def test_fp8_empty_inputs_are_valid_noops():
 
 # ------------------------------------------------------- attn_decode_noalloc
 @pytest.mark.parametrize("kw,status", [
-    (dict(q=0), NULL), (dict(dtype=1), UNSUP), (dict(d=80), UNSUP), (dict(Hkv=3), SHAPE),
+    (dict(q=0), NULL), (dict(dtype=1), UNSUP), (dict(d=96), UNSUP), (dict(Hkv=3), SHAPE),
     (dict(q=P + 2), LAYOUT), (dict(B=64, Lmax=40_000_000), UNSUP),
 ])
 def test_decode_noalloc_rejections(kw, status):

@@ -32,7 +32,7 @@ def run_decode(w, dev, lengths=None, poison=True, scale=None):
 EDGE_LENGTHS = [0, 1, 2, 31, 32, 33, 127, 128, 129, 511, 512, 513, 1023, 1100]
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 80, 128])
 @pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 4), (32, 8), (20, 1), (40, 2)])
 def test_decode_small(dev, d, Hq, Hkv):
     B = len(EDGE_LENGTHS)
@@ -42,7 +42,7 @@ def test_decode_small(dev, d, Hq, Hkv):
     assert (o[0] == 0).all().item() and torch.isneginf(lse[0]).all().item()
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 80, 128])
 def test_decode_many_short_sequences(dev, d):
     """300 sequences of 0..200 slots (every 17th empty): the split kernel's
     prefix sums over the lengths take five 64-sequence passes, and one piece
@@ -79,9 +79,12 @@ def test_decode_empty_cache(dev):
     assert (o == 0).all().item() and torch.isneginf(lse).all().item()
 
 
-def test_decode_strided_cache(dev):
-    """Cache stored [B, Lmax, Hkv, d] and viewed as [B, Hkv, Lmax, d]."""
-    B, Hq, Hkv, Lmax, d = 5, 8, 2, 700, 128
+@pytest.mark.parametrize("d", [80, 128])
+def test_decode_strided_cache(dev, d):
+    """Cache stored [B, Lmax, Hkv, d] and viewed as [B, Hkv, Lmax, d]: at
+    head_dim 80 a row is 160 bytes and the next kv head's row follows it, so
+    a read past head_dim would take that row's values."""
+    B, Hq, Hkv, Lmax = 5, 8, 2, 700
     g = torch.Generator().manual_seed(21)
     q = torch.randn(B, Hq, d, generator=g).to(torch.bfloat16)
     ks = torch.randn(B, Lmax, Hkv, d, generator=g).to(torch.bfloat16)
@@ -91,7 +94,7 @@ def test_decode_strided_cache(dev):
                               lens.to(dev))
     torch.cuda.synchronize()
     o_ref, lse_ref = orc.attention_decode(q, ks.transpose(1, 2), vs.transpose(1, 2), lens.numpy())
-    check(to_np(o), o_ref, to_np(lse), lse_ref, "bf16", "decode strided cache")
+    check(to_np(o), o_ref, to_np(lse), lse_ref, "bf16", f"decode strided cache d{d}")
 
 
 def test_decode_equals_last_row_of_causal_prefill_on_gpu(dev):

@@ -149,7 +149,7 @@ def test_sweep_bwd(dev, case):
 @pytest.mark.parametrize("case", range(N_CASES))
 def test_sweep_decode(dev, case):
     r = np.random.default_rng(5500 + case)
-    d = int(r.choice([64, 128]))
+    d = int(r.choice([64, 80, 128]))
     Hkv = int(r.integers(1, 4))
     group = int(r.choice([1, 2, 4, 8, 20]))
     B = int(r.integers(1, 7))
