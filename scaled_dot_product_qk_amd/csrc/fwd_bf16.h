@@ -161,10 +161,9 @@ struct Bf16FwdShape {
 };
 
 // Key/value tile buffers in LDS: three for the pipelined schedule (head_dim
-// 64, not causal, no mask; there a tile's V operands are read after the
+// 64, no mask, causal or not; there a tile's V operands are read after the
 // barrier at which the copies of the tile two ahead are issued), two
-// otherwise.  (The causal instance would need more than 256 registers per
-// lane for the pipeline: its diagonal tiles' masking spills Q's operands.)
+// otherwise.
 __host__ __device__ constexpr int bf16_fwd_kv_stages(int d, bool causal, int mk) {
   return d == 64 && mk == 0 ? 3 : 2;
 }
@@ -448,7 +447,7 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
   // reference max, see kSumGuard), so that the products of one half can run
   // on the matrix core while the vector ALU forms the softmax of another.
   //
-  // Head_dim 64, not causal, no mask (kPipe): a software pipeline across
+  // Head_dim 64, no mask, causal or not (kPipe): a software pipeline across
   // tiles.  With S(t, h) the scores of half h of tile t and PV(t, h) its
   // O^T += V^T P^T products,
   //
@@ -463,9 +462,14 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
   // read at the end of phase B, after the barrier of tile t: with three LDS
   // buffers, tile t's buffer is refilled only after the barrier of tile t + 1.
   //
-  // The other instances (head_dim 80 and 128, causal, masked) keep both
-  // softmax halves of a tile before its barrier, which needs fewer registers
-  // and, with a mask, keeps the mask words of the tile readable from LDS:
+  // Causal, every wave runs every key tile of its workgroup, the tiles on
+  // the diagonal masked inside the pipeline (fused_half with MASK), so that
+  // no wave leaves the shared schedule early.
+  //
+  // The other instances (head_dim 80 and 128, and every masked one) keep
+  // both softmax halves of a tile before its barrier, which needs fewer
+  // registers and, with a mask, keeps the mask words of the tile readable
+  // from LDS:
   //
   //   S(t, 0) | S(t, 1) + softmax(t, 0) | PV(t, 0) + softmax(t, 1) | barrier | PV(t, 1)
   u32x4 ka_next[S::kKC];     // K operands, first key half of the next tile
