@@ -823,12 +823,40 @@ attn_fwd_bf16_kernel(FwdParams p_in) {
     // the last one or two of them run with the masked path, which is exact
     // for them as well.
     int t = 0;
+    // Not causal (every work item the same size): the wave priority falls
+    // with the share of the key tiles done (3 in the first quarter, 0 in the
+    // last), so on a SIMD shared by two workgroups the wave with more work
+    // left issues first.  Left to the age order (oldest wave first), the
+    // first workgroup on each compute unit ran its tiles 1.6x as fast as the
+    // second, the two drifted apart, and the last round of work items ended
+    // up to 90 us apart across compute units (34 us with the priority).
+    // Causal items differ in size, and the same rule slowed them.
+    int prio = 4;
+    auto lower_prio = [&](int t) __attribute__((always_inline)) {
+      if constexpr (!CAUSAL) {
+        const int want = 3 - min(3, (4 * t) / max(n_tiles, 1));
+        if (want < prio) {
+          prio = want;
+          switch (want) {
+            case 3: __builtin_amdgcn_s_setprio(3); break;
+            case 2: __builtin_amdgcn_s_setprio(2); break;
+            case 1: __builtin_amdgcn_s_setprio(1); break;
+            default: __builtin_amdgcn_s_setprio(0); break;
+          }
+        }
+      }
+    };
     for (; t + 3 <= n_plain; t += 3) {
+      lower_prio(t);
       step(std::false_type{}, t, std::integral_constant<int, 0>{});
       step(std::false_type{}, t + 1, std::integral_constant<int, 1>{});
       step(std::false_type{}, t + 2, std::integral_constant<int, 2>{});
     }
-    for (; t < n_tiles; ++t) step(std::true_type{}, t, std::integral_constant<int, -1>{});
+    for (; t < n_tiles; ++t) {
+      lower_prio(t);
+      step(std::true_type{}, t, std::integral_constant<int, -1>{});
+    }
+    if constexpr (!CAUSAL) __builtin_amdgcn_s_setprio(0);
   } else {
     auto step = [&](auto mask_tag, int t) __attribute__((always_inline)) {
       const bool act = active(t);
