@@ -58,9 +58,12 @@ __device__ __forceinline__ f32x4 mfma16_fp8(const u32x8& a, const u32x8& b, cons
                                                           c, 0, 0, 0, 127, 0, 127);
 }
 
-// Four fp32 values to e4m3 codes (nearest even) packed low byte first.
+// Four fp32 values to e4m3 codes (nearest even) packed low byte first.  The
+// first conversion writes the low half-word and keeps the high one of the
+// word it is given, which the second conversion overwrites: any word will
+// do, and a's bits (dead after this) save the zeroing a literal 0 costs.
 __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }
