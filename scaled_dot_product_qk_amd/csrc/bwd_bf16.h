@@ -13,9 +13,10 @@
 //     (each row read by a group of adjacent lanes, whole rows per load);
 //   * attn_bwd_dkdv_kernel: one workgroup per (batch, kv head, 128 keys); each
 //     key group of 32 keeps its K and V in registers and walks the 32-query
-//     tiles of the group's query heads (Q, dO and the row statistics copied
-//     straight into LDS), so dK and dV of a grouped head are summed without
-//     atomics;
+//     tiles of the group's query heads (Q, dO and the row statistics staged
+//     through registers into LDS), so dK and dV of a grouped head are summed
+//     without atomics; at head_dim 128 two waves serve a key group, one
+//     forming P and dV, the other dS and dK;
 //   * attn_bwd_dq_kernel: one workgroup per (batch, query head, 128 queries);
 //     each wave keeps its 32 queries' Q, dO, LSE and D in registers and walks
 //     32-key tiles of K and V copied straight into LDS.
@@ -104,37 +105,46 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- dK, dV
-// Largest Q, dO, K, V token stride (elements) the backward's copies allow: a
-// lane's 32-bit offset spans up to 31 rows of one 32-row tile.
+// Largest K, V token stride (elements) the dQ kernel's copies allow: a lane's
+// 32-bit offset spans up to 31 rows of one 32-row tile.  (Q and dO are held
+// to the same bound.)
 constexpr int64_t kBwdMaxTokenStride = int64_t(1) << 26;
 
-// dK/dV workgroup: 128 keys in 4 groups of 32; at head_dim 128 every group is
-// served by two waves that each own half of head_dim for dK and dV (and both
-// form the group's S and dP), so that a wave needs no more than 256
-// registers and two waves share each SIMD.  Q and dO tiles of 32 rows and
-// the rows' (LSE log2 e, D) pairs are copied straight into LDS, four steps in
-// flight.
+// dK/dV workgroup: 128 keys in 4 groups of 32.  Below head_dim 128 one wave
+// serves each group and forms S, dP, P, dS and both gradients.  At head_dim
+// 128 that would need more than 256 registers, so each group is served by
+// two waves that split the work by gradient: the P wave forms S = Q K^T and
+// P, hands P to its partner through LDS and accumulates dV; the dS wave
+// forms dP = dO V^T, and after the next barrier takes P, forms dS and
+// accumulates dK.  Each product is formed once, and the two waves of a group
+// have the same matrix work per step.  Q and dO tiles of 32 rows and the
+// rows' (LSE log2 e, D) pairs are loaded into registers and written to LDS
+// two steps ahead of the one computed (direct global-to-LDS copies made this
+// kernel about a fifth slower).
 template <int D>
 struct BwdKvShape {
-  static constexpr int kSplit = D == 128 ? 2 : 1;
-  static constexpr int kWaves = 4 * kSplit;
+  static constexpr bool kRoles = D == 128;
+  static constexpr int kWaves = kRoles ? 8 : 4;
   static constexpr int kKC = D / 16;                  // k-slices over head_dim
   static constexpr int kND = (D + 31) / 32;           // 32-row head_dim blocks (the last padded at d = 80)
-  static constexpr int kNDW = kND / kSplit;           // ... per wave
   static constexpr int kChunks = D / 8;               // 16-byte chunks of a row in memory
   static constexpr int kPitch = D <= 64 ? 8 : 16;     // 16-byte chunks of a row in LDS
   static constexpr int kRowBytes = 16 * kPitch;
   static constexpr int kTileBytes = kBwdRows * kRowBytes;
   static constexpr int kStatBytes = kBwdRows * 8;
   static constexpr int kStageBytes = 2 * kTileBytes + kStatBytes;  // Q, dO, statistics
+  // Four buffers: a step's tiles are written two steps ahead, and the dS wave
+  // reads a step's Q tile after the next barrier.
   static constexpr int kStages = 4;
-  static constexpr int kLdsBytes = kStages * kStageBytes;
+  static constexpr int kPBytes = 64 * 16 * 4;         // one group's fp32 P tile, 16 values per lane
+  static constexpr int kXchgBytes = kRoles ? 2 * 4 * kPBytes : 0;  // two slots per key group
+  static constexpr int kLdsBytes = kStages * kStageBytes + kXchgBytes;
   static constexpr int kRowsPerCopy = 1024 / kRowBytes;
   static constexpr int kCopiesPerTile = kBwdRows / kRowsPerCopy;
   static constexpr int kCopiesPerWave = 2 * kCopiesPerTile / kWaves;  // plus the statistics for wave 0
   static_assert(kCopiesPerWave * kWaves == 2 * kCopiesPerTile, "copies split evenly over the waves");
   static_assert(kCopiesPerTile % kCopiesPerWave == 0, "a wave copies from one tile only");
-  static_assert(kND % kSplit == 0 && kChunks <= kPitch, "head_dim blocks split evenly; rows fit their pitch");
+  static_assert(kChunks <= kPitch, "rows fit their pitch");
 };
 
 // LDS layout of a staged Q or dO row r: 16-byte chunk c at c ^ bwd_swz(r).
@@ -153,13 +163,19 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   using S = BwdKvShape<D>;
   typedef __attribute__((address_space(3))) char lds_char;
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_raw[];
   lds_char* const lds = (lds_char*)lds_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, ln = lane & 31;
-  const int kgrp = wave & 3, dpart = wave >> 2;
+  const int kgrp = wave & 3;
+  // With two roles, waves 0-3 are the P waves (dV) and 4-7 the dS waves (dK).
+  const bool ds_wave = S::kRoles && wave >= 4;
+  const bool p_wave = !ds_wave;
+  const bool do_dv = !S::kRoles || p_wave, do_dk = !S::kRoles || ds_wave;
   // Key blocks slowest (heaviest first when causal), (batch, kv head)
   // fastest, so that the key blocks of one kv head run on one XCD.
   const int n_bh = p.B * p.Hkv;
@@ -169,24 +185,31 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
   const int wave_k0 = k0 + 32 * kgrp;
   const int key = wave_k0 + ln;  // this lane's key column
 
-  // K^T and V^T as B operands of S = Q K^T and dP = dO V^T: lane holds row
-  // `key` of K (V), head-dim 16 kc + 8 g .. +8.  Keys past Lk are zero.
-  u32x4 kop[S::kKC], vop[S::kKC];
+  // K^T (P wave) and V^T (dS wave) as B operands of S = Q K^T and dP = dO V^T:
+  // lane holds row `key` of K (V), head-dim 16 kc + 8 g .. +8.  Keys past Lk
+  // are zero.  A single wave holds both.
+  u32x4 kop[S::kKC], vop[S::kRoles ? 1 : S::kKC];
   {
-    const uint16_t* kr = reinterpret_cast<const uint16_t*>(p.k) + b * p.k_sb + hk * p.k_sh + (int64_t)key * p.k_st;
-    const uint16_t* vr = reinterpret_cast<const uint16_t*>(p.v) + b * p.v_sb + hk * p.v_sh + (int64_t)key * p.v_st;
     const bool ok = key < p.Lk;
+    const uint16_t* kr = reinterpret_cast<const uint16_t*>(ds_wave ? p.v : p.k) +
+                         b * (ds_wave ? p.v_sb : p.k_sb) + hk * (ds_wave ? p.v_sh : p.k_sh) +
+                         (int64_t)key * (ds_wave ? p.v_st : p.k_st);
 #pragma unroll
-    for (int kc = 0; kc < S::kKC; ++kc) {
-      kop[kc] = ok ? load16(kr + 16 * kc + 8 * g) : zero16();
-      vop[kc] = ok ? load16(vr + 16 * kc + 8 * g) : zero16();
+    for (int kc = 0; kc < S::kKC; ++kc) kop[kc] = ok ? load16(kr + 16 * kc + 8 * g) : zero16();
+    if constexpr (!S::kRoles) {
+      const uint16_t* vr = reinterpret_cast<const uint16_t*>(p.v) + b * p.v_sb + hk * p.v_sh + (int64_t)key * p.v_st;
+#pragma unroll
+      for (int kc = 0; kc < S::kKC; ++kc) vop[kc] = ok ? load16(vr + 16 * kc + 8 * g) : zero16();
     }
   }
-  f32x16 dk_acc[S::kNDW], dv_acc[S::kNDW];
+  // Accumulators over head_dim blocks: dV^T then dK^T for a single wave; the
+  // P wave's dV^T or the dS wave's dK^T with two roles.
+  constexpr int kAcc = S::kRoles ? S::kND : 2 * S::kND;
+  f32x16 acc[kAcc];
 #pragma unroll
-  for (int i = 0; i < S::kNDW; ++i)
+  for (int i = 0; i < kAcc; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dk_acc[i][r] = dv_acc[i][r] = 0.f;
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
   // Steps: query tiles from the last down to the first one with a query at
   // or after k0 (causal), the group's query heads within each tile, so that
@@ -196,72 +219,72 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
   const int n_steps = p.group * (n_qt - qt_lo);
   const float c = p.scale_log2;
 
-  // ---- copy plan: wave w issues copies kCopiesPerWave * w .. +kCopiesPerWave-1
-  // of a step (Q tile copies first, then dO); copy ci fills tile rows
-  // kRowsPerCopy * (ci % kCopiesPerTile) ..; lane -> row lane / kPitch,
-  // physical chunk lane % kPitch.  Wave 0 also copies the statistics.
+  // ---- copy plan: wave w moves chunks kCopiesPerWave * w .. +kCopiesPerWave-1
+  // of a step (Q tile first, then dO); chunk ci covers tile rows
+  // kRowsPerCopy * (ci % kCopiesPerTile) ..; lane -> row lane / kPitch, 16-byte
+  // chunk lane % kPitch of the row, read in memory order and written to its
+  // swizzled LDS slot.  Wave 0 also moves the statistics.  Each step's data
+  // is loaded into registers two steps before it is written to LDS, so that
+  // its loads have that long to land.
   const int ci0 = S::kCopiesPerWave * wave;
   const bool cp_q = ci0 < S::kCopiesPerTile;
   const int cp_row0 = S::kRowsPerCopy * (ci0 % S::kCopiesPerTile);
-  uint32_t cp_rel[S::kCopiesPerWave];   // byte offset of the lane's chunk within its row
+  const int cp_c = lane % S::kPitch;                // chunk of the row in memory
+  const bool cp_on = S::kChunks == S::kPitch || cp_c < S::kChunks;  // padding chunks (head_dim 80) load nothing
   int cp_row[S::kCopiesPerWave];        // tile row of the lane
-  int cp_lc[S::kCopiesPerWave];         // slots of padding chunks (head_dim 80) stay idle
+  uint32_t cp_dst[S::kCopiesPerWave];   // LDS byte offset of the lane's slot within the stage
 #pragma unroll
   for (int j = 0; j < S::kCopiesPerWave; ++j) {
     const int r = cp_row0 + S::kRowsPerCopy * j + lane / S::kPitch;
     cp_row[j] = r;
-    cp_lc[j] = (lane % S::kPitch) ^ bwd_swz<S::kPitch>(r);  // logical chunk of the lane's slot
-    cp_rel[j] = 16u * (uint32_t)cp_lc[j];
+    cp_dst[j] = (cp_q ? 0 : S::kTileBytes) + r * S::kRowBytes + 16 * (cp_c ^ bwd_swz<S::kPitch>(r));
   }
   const int64_t cp_st = cp_q ? p.q_st : p.do_st;
-  const uint32_t cp_row_bytes = (uint32_t)(2 * cp_st);  // < 2^27: token strides are validated
-  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  const int64_t cp_sh = cp_q ? p.q_sh : p.do_sh;
   // Step st is query head hg = st % group of query tile n_qt - 1 - st / group.
-  // The copies and the compute visit the steps in order, so each keeps a
-  // cursor (head within the group, query tile) advanced by one step at a time
-  // instead of dividing by the runtime group size, a sequence of some twenty
-  // scalar instructions (the backward ran 3 % faster without the two
-  // divisions per step).
-  int iss_hg = 0, iss_qt = n_qt - 1;  // next step to copy
-  auto issue_step = [&](int st) {
-    const int hg = iss_hg, qt = iss_qt;
+  // The loads and the compute visit the steps in order, so each keeps a
+  // cursor (head within the group, query tile, source rows) advanced one step
+  // at a time instead of dividing by the runtime group size and multiplying
+  // out the strides.
+  int iss_hg = 0, iss_qt = n_qt - 1;  // next step to load
+  const uint16_t* iss_src = (cp_q ? reinterpret_cast<const uint16_t*>(p.q) + b * p.q_sb
+                                  : reinterpret_cast<const uint16_t*>(p.dout) + b * p.do_sb) +
+                            (int64_t)(hk * p.group) * cp_sh + (int64_t)(iss_qt * kBwdRows) * cp_st;
+  const int64_t iss_wrap = (int64_t)p.group * cp_sh + kBwdRows * cp_st;
+  const float* iss_stat = p.stats + 2 * (((int64_t)b * p.Hq + hk * p.group) * p.Lq + iss_qt * kBwdRows);
+  const int64_t stat_sh = 2 * (int64_t)p.Lq, stat_wrap = 2 * ((int64_t)p.group * p.Lq + kBwdRows);
+  struct Staged {
+    u32x4 v[S::kCopiesPerWave];
+    float st;
+  };
+  auto load_step = [&](Staged& x) __attribute__((always_inline)) {
+    const int r0 = iss_qt * kBwdRows;
+    const uint16_t* src = iss_src;
+    const float* st_src = iss_stat;
+    iss_src += cp_sh;
+    iss_stat += stat_sh;
     if (++iss_hg == p.group) {
       iss_hg = 0;
       --iss_qt;
+      iss_src -= iss_wrap;
+      iss_stat -= stat_wrap;
     }
-    const int h = hk * p.group + hg;
-    const int r0 = qt * kBwdRows;
-    const uint32_t dst = lds0 + (st % S::kStages) * S::kStageBytes + (cp_q ? 0 : S::kTileBytes);
-    const uint16_t* src = cp_q ? reinterpret_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh
-                               : reinterpret_cast<const uint16_t*>(p.dout) + b * p.do_sb + h * p.do_sh;
-    src += (int64_t)r0 * cp_st;
 #pragma unroll
     for (int j = 0; j < S::kCopiesPerWave; ++j) {
       const int row = min(r0 + cp_row[j], p.Lq - 1) - r0;  // rows past Lq repeat the last one
-      if (S::kChunks == S::kPitch || cp_lc[j] < S::kChunks)
-        lds_copy16(src, (uint32_t)row * cp_row_bytes + cp_rel[j],
-                   dst + (cp_row0 + S::kRowsPerCopy * j) * S::kRowBytes);
+      x.v[j] = cp_on ? load16(src + (int64_t)row * cp_st + 8 * cp_c) : zero16();
     }
     if (wave == 0) {
-      const float* st_src = p.stats + 2 * (((int64_t)b * p.Hq + h) * p.Lq + r0);
       const int row = min(r0 + (lane >> 1), p.Lq - 1) - r0;
-      lds_copy4(st_src, (uint32_t)(8 * row + 4 * (lane & 1)),
-                lds0 + (st % S::kStages) * S::kStageBytes + 2 * S::kTileBytes);
+      x.st = st_src[2 * row + (lane & 1)];
     }
   };
-  // Waits until at most `pending` later steps' copies of this wave are in flight.
-  auto wait_steps = [&](int pending) {
-    if (wave == 0) {
-      constexpr int n = S::kCopiesPerWave + 1;
-      if (pending >= 2) __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * n));
-      else if (pending == 1) __builtin_amdgcn_s_waitcnt(0x0f70 | n);
-      else __builtin_amdgcn_s_waitcnt(0x0f70);
-    } else {
-      constexpr int n = S::kCopiesPerWave;
-      if (pending >= 2) __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * n));
-      else if (pending == 1) __builtin_amdgcn_s_waitcnt(0x0f70 | n);
-      else __builtin_amdgcn_s_waitcnt(0x0f70);
-    }
+  auto write_step = [&](const Staged& x, int buf) __attribute__((always_inline)) {
+    lds_char* stage = lds + buf * S::kStageBytes;
+#pragma unroll
+    for (int j = 0; j < S::kCopiesPerWave; ++j) *reinterpret_cast<lds_u32x4*>(stage + cp_dst[j]) = x.v[j];
+    if (wave == 0)
+      *reinterpret_cast<__attribute__((address_space(3))) float*>(stage + 2 * S::kTileBytes + 4 * lane) = x.st;
   };
 
   // ---- LDS operand offsets within a tile ----
@@ -290,17 +313,108 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
     const uint32_t a0 = l2[0], a1 = l2[1], a2 = h2[0], a3 = h2[1];
     return u32x4{a0, a1, a2, a3};
   };
-
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): K and V have landed before the copies start
+  // A product of 32 rows (the stage's Q or dO tile) with this lane's key
+  // operands: S = Q K^T, dP = dO V^T; rows = the tile's queries, columns = keys.
+  auto row_product = [&](const lds_char* tile, const u32x4* bop) __attribute__((always_inline)) {
+    f32x16 acc_s;
 #pragma unroll
-  for (int st = 0; st < S::kStages - 1; ++st)
-    if (st < n_steps) issue_step(st);
+    for (int r = 0; r < 16; ++r) acc_s[r] = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < S::kKC; ++kc) {
+      const u32x4 a = *reinterpret_cast<const lds_u32x4*>(tile + (rd_off ^ (32 * kc)));
+      acc_s = mfma32(a, bop[kc], acc_s);
+    }
+    return acc_s;
+  };
+  // Statistics of the rows this lane's accumulator registers hold: row
+  // 8 (r / 4) + 4 g + r % 4 of the tile; element 0 is LSE log2 e, 1 is D.
+  auto row_stats = [&](const lds_char* stage, int r, int e) __attribute__((always_inline)) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) float*>(
+        stage + 2 * S::kTileBytes + 8 * (8 * (r >> 2) + 4 * g + (r & 3)) + 4 * e);
+  };
+  // P = exp2(c S - LSE log2 e), zero for pairs that do not take part (rows
+  // past Lq, keys past Lk, causal keys after the query).
+  auto probs = [&](const f32x16& s, const lds_char* stage, int r0, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    f32x16 pe;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qrow = r0 + 8 * (r >> 2) + 4 * g + (r & 3);
+      const bool vis = !MASK || (qrow < p.Lq && key < p.Lk && (!CAUSAL || key <= qrow));
+      const float pv = fast_exp2(__builtin_fmaf(s[r], c, -row_stats(stage, r, 0)));
+      pe[r] = vis ? pv : 0.f;
+    }
+    return pe;
+  };
+  // Packs 16 accumulator values as the B operands of the two 16-query slices.
+  auto pack_b = [&](const f32x16& x, u32x4* out) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cs = 0; cs < 2; ++cs)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[cs][j] = pack_bf16x2(x[8 * cs + 2 * j], x[8 * cs + 2 * j + 1]);
+  };
+  // dV^T (dK^T) += X^T B over head-dim blocks first .. first + n - 1, X the
+  // stage's dO (Q) tile read transposed.
+  auto grad_product = [&](const lds_char* tile, const u32x4* bsl, int acc0, int first, int n) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < n; ++i)
+#pragma unroll
+      for (int cs = 0; cs < 2; ++cs) acc[acc0 + i] = mfma32(tr_read(tile, first + i, cs), bsl[cs], acc[acc0 + i]);
+  };
+  // Fully visible tiles (all rows below Lq, all keys below Lk and, causal,
+  // every query at or after the wave's last key) skip the per-pair test,
+  // which is most of them.
+  auto all_visible = [&](int r0) {
+    return r0 + kBwdRows <= p.Lq && wave_k0 + 32 <= p.Lk && (!CAUSAL || r0 >= wave_k0 + 31);
+  };
 
-  int cmp_hg = 0, cmp_qt = n_qt - 1;  // this step's cursor
+  // Steps 0 and 1 go straight to LDS; 2 and 3 wait in registers.
+  Staged stg_a{}, stg_b{};
+  if (n_steps > 0) {
+    load_step(stg_a);
+    write_step(stg_a, 0);
+  }
+  if (n_steps > 1) {
+    load_step(stg_a);
+    write_step(stg_a, 1);
+  }
+  if (n_steps > 2) load_step(stg_a);
+  if (n_steps > 3) load_step(stg_b);
+
+  // P exchange (two roles): slot (step & 1) of this key group, lane-major
+  // 16-byte chunks, chunk j of lane l at 16 (64 j + l).
+  lds_char* const xchg = lds + S::kStages * S::kStageBytes + kgrp * 2 * S::kPBytes;
+  int prev_buf = -1;  // dS wave: buffer of the previous step (-1: nothing to finish)
+  // dS wave, for the previous step (its tiles still in their buffer, its P
+  // left by the P wave before this barrier): dP = dO V^T, dS = P (dP - D),
+  // dK^T += Q^T dS.
+  auto finish_prev = [&](int slot) __attribute__((always_inline)) {
+    const lds_char* stage = lds + prev_buf * S::kStageBytes;
+    const f32x16 dp = row_product(stage + S::kTileBytes, kop);
+    f32x16 ds;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 pv = *reinterpret_cast<const lds_f32x4*>(xchg + slot * S::kPBytes + 16 * (64 * j + lane));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ds[4 * j + e] = pv[e] * (dp[4 * j + e] - row_stats(stage, 4 * j + e, 1));
+    }
+    u32x4 dsb[2];
+    pack_b(ds, dsb);
+    grad_product(stage, dsb, 0, 0, S::kND);
+  };
+
+  int cmp_hg = 0, cmp_qt = n_qt - 1, cmp_buf = 0;  // this step's cursor
   for (int step = 0; step < n_steps; ++step) {
-    wait_steps(min(S::kStages - 2, n_steps - 1 - step));
-    __syncthreads();  // step's tiles in LDS; every wave is done with step - 1's buffer
-    if (step + S::kStages - 1 < n_steps) issue_step(step + S::kStages - 1);
+    const int buf = cmp_buf;
+    cmp_buf = cmp_buf == S::kStages - 1 ? 0 : cmp_buf + 1;
+    __syncthreads();  // step's tiles in LDS; every wave is done with the buffer refilled next
+    // Step + 2 from registers into its buffer (free since step - 2), then the
+    // loads of step + 4.
+    if (step + 2 < n_steps) write_step(stg_a, buf + 2 < S::kStages ? buf + 2 : buf + 2 - S::kStages);
+    stg_a = stg_b;
+    if (step + 4 < n_steps) load_step(stg_b);
+    if (ds_wave && prev_buf >= 0) finish_prev((step - 1) & 1);
+    prev_buf = -1;
     const int qt = cmp_qt;
     if (++cmp_hg == p.group) {
       cmp_hg = 0;
@@ -309,92 +423,61 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
     const int r0 = qt * kBwdRows;
     // A wave whose keys all come after the tile's last query has nothing here.
     if (!CAUSAL || r0 + kBwdRows - 1 >= wave_k0) {
-      const lds_char* qt_l = lds + (step % S::kStages) * S::kStageBytes;
-      const lds_char* dt_l = qt_l + S::kTileBytes;
-      const float* st_l = (const float*)(qt_l + 2 * S::kTileBytes);
-      // S = Q K^T and dP = dO V^T: rows = the tile's 32 queries, columns = keys.
-      f32x16 s, dp;
+      if (ds_wave) {
+        prev_buf = buf;
+      } else {
+        // P wave, or a single wave.
+        const lds_char* stage = lds + buf * S::kStageBytes;
+        const lds_char* qt_l = stage;
+        const lds_char* dt_l = stage + S::kTileBytes;
+        const f32x16 s = row_product(qt_l, kop);
+        const f32x16 pe =
+            all_visible(r0) ? probs(s, stage, r0, std::false_type{}) : probs(s, stage, r0, std::true_type{});
+        u32x4 pb[2];
+        pack_b(pe, pb);
+        if constexpr (S::kRoles) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<lds_f32x4*>(xchg + (step & 1) * S::kPBytes + 16 * (64 * j + lane)) =
+                f32x4{pe[4 * j], pe[4 * j + 1], pe[4 * j + 2], pe[4 * j + 3]};
+          grad_product(dt_l, pb, 0, 0, S::kND);
+        } else {
+          const f32x16 dp = row_product(dt_l, vop);
+          f32x16 ds;
 #pragma unroll
-      for (int kc = 0; kc < S::kKC; ++kc) {
-        const u32x4 qa = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(qt_l + (rd_off ^ (32 * kc)));
-        const u32x4 da = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(dt_l + (rd_off ^ (32 * kc)));
-        s = mfma32(qa, kop[kc], s);
-        dp = mfma32(da, vop[kc], dp);
+          for (int r = 0; r < 16; ++r) ds[r] = pe[r] * (dp[r] - row_stats(stage, r, 1));
+          u32x4 dsb[2];
+          pack_b(ds, dsb);
+          grad_product(dt_l, pb, 0, 0, S::kND);
+          grad_product(qt_l, dsb, S::kND, 0, S::kND);
+        }
       }
-      // P = exp2(c S - LSE log2 e), dS = P (dP - D), packed as the B operands
-      // of the two 16-query slices; rows 8 (r / 4) + 4 g + r % 4.  Tiles whose
-      // every (query, key) pair of the wave takes part (all rows below Lq and,
-      // causal, every query at or after the wave's last key) skip the
-      // per-pair test, which is most of them.
-      u32x4 pb[2], dsb[2];
-      const bool all_vis = r0 + kBwdRows <= p.Lq && wave_k0 + 32 <= p.Lk && (!CAUSAL || r0 >= wave_k0 + 31);
-      auto probs = [&](auto mask_tag) __attribute__((always_inline)) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-#pragma unroll
-        for (int cs = 0; cs < 2; ++cs) {
-          float pe[8], de[8];
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const int rb = 8 * (2 * cs + jj) + 4 * g;  // first of 4 consecutive rows
-            const f32x4 s01 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-                (const lds_char*)st_l + 8 * rb);
-            const f32x4 s23 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-                (const lds_char*)st_l + 8 * rb + 16);
-            const float l2v[4] = {s01[0], s01[2], s23[0], s23[2]};
-            const float dlv[4] = {s01[1], s01[3], s23[1], s23[3]};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 8 * cs + 4 * jj + e;
-              const int qrow = r0 + rb + e;
-              const bool vis = !MASK || (qrow < p.Lq && key < p.Lk && (!CAUSAL || key <= qrow));
-              const float pv = vis ? fast_exp2(__builtin_fmaf(s[r], c, -l2v[e])) : 0.f;
-              pe[4 * jj + e] = pv;
-              de[4 * jj + e] = pv * (dp[r] - dlv[e]);
-            }
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            pb[cs][j] = pack_bf16x2(pe[2 * j], pe[2 * j + 1]);
-            dsb[cs][j] = pack_bf16x2(de[2 * j], de[2 * j + 1]);
-          }
-        }
-      };
-      if (all_vis)
-        probs(std::false_type{});
-      else
-        probs(std::true_type{});
-      // dV^T += dO^T P and dK^T += Q^T dS over this wave's head_dim blocks.
-#pragma unroll
-      for (int i = 0; i < S::kNDW; ++i)
-#pragma unroll
-        for (int cs = 0; cs < 2; ++cs) {
-          const int db = dpart * S::kNDW + i;
-          dv_acc[i] = mfma32(tr_read(dt_l, db, cs), pb[cs], dv_acc[i]);
-          dk_acc[i] = mfma32(tr_read(qt_l, db, cs), dsb[cs], dk_acc[i]);
-        }
     }
+  }
+  if constexpr (S::kRoles) {
+    __syncthreads();  // the last step's P is in LDS
+    if (ds_wave && prev_buf >= 0) finish_prev((n_steps - 1) & 1);
   }
 
   // dK = scale dK_acc, dV = dV_acc: lane = key, registers = head-dim rows.
   if (key < p.Lk) {
     uint16_t* dkr = reinterpret_cast<uint16_t*>(p.dk) + b * p.dk_sb + hk * p.dk_sh + (int64_t)key * p.dk_st;
     uint16_t* dvr = reinterpret_cast<uint16_t*>(p.dv) + b * p.dv_sb + hk * p.dv_sh + (int64_t)key * p.dv_st;
+    auto store = [&](uint16_t* row, int a0, float mul) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < S::kNDW; ++i)
+      for (int i = 0; i < S::kND; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = 32 * (dpart * S::kNDW + i) + 8 * j + 4 * g;
-        if (d >= D) continue;  // padding rows of the last block (head_dim 80)
-        u32x2 wk, wv;
-        wk[0] = pack_bf16x2(dk_acc[i][4 * j + 0] * p.scale, dk_acc[i][4 * j + 1] * p.scale);
-        wk[1] = pack_bf16x2(dk_acc[i][4 * j + 2] * p.scale, dk_acc[i][4 * j + 3] * p.scale);
-        wv[0] = pack_bf16x2(dv_acc[i][4 * j + 0], dv_acc[i][4 * j + 1]);
-        wv[1] = pack_bf16x2(dv_acc[i][4 * j + 2], dv_acc[i][4 * j + 3]);
-        *reinterpret_cast<u32x2*>(dkr + d) = wk;
-        *reinterpret_cast<u32x2*>(dvr + d) = wv;
-      }
+        for (int j = 0; j < 4; ++j) {
+          const int d = 32 * i + 8 * j + 4 * g;
+          if (d >= D) continue;  // padding rows of the last block (head_dim 80)
+          u32x2 w;
+          w[0] = pack_bf16x2(acc[a0 + i][4 * j + 0] * mul, acc[a0 + i][4 * j + 1] * mul);
+          w[1] = pack_bf16x2(acc[a0 + i][4 * j + 2] * mul, acc[a0 + i][4 * j + 3] * mul);
+          *reinterpret_cast<u32x2*>(row + d) = w;
+        }
+    };
+    if (do_dv) store(dvr, 0, 1.f);
+    if (do_dk) store(dkr, S::kRoles ? 0 : S::kND, p.scale);
   }
 }
 
