@@ -133,8 +133,15 @@ struct BwdKvShape {
   static constexpr int kTileBytes = kBwdRows * kRowBytes;
   static constexpr int kStatBytes = kBwdRows * 8;
   static constexpr int kStageBytes = 2 * kTileBytes + kStatBytes;  // Q, dO, statistics
-  // Four buffers: a step's tiles are written two steps ahead, and the dS wave
-  // reads a step's Q tile after the next barrier.
+  // Tile copies.  With two roles they are staged through registers: loaded
+  // two steps before they are written to LDS, written two steps ahead of the
+  // one computed (direct global-to-LDS copies made that kernel about a fifth
+  // slower).  A single wave copies straight into LDS, three steps ahead: its
+  // registers have no room for staging, and there the direct copies measured
+  // faster.  Four buffers either way; with two roles the dS wave reads a
+  // step's Q tile after the next barrier.
+  static constexpr bool kStaged = kRoles;
+  static constexpr int kAhead = 3;  // direct copies: steps in flight beyond the one computed
   static constexpr int kStages = 4;
   static constexpr int kPBytes = 64 * 16 * 4;         // one group's fp32 P tile, 16 values per lane
   static constexpr int kXchgBytes = kRoles ? 2 * 4 * kPBytes : 0;  // two slots per key group
@@ -221,46 +228,42 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
 
   // ---- copy plan: wave w moves chunks kCopiesPerWave * w .. +kCopiesPerWave-1
   // of a step (Q tile first, then dO); chunk ci covers tile rows
-  // kRowsPerCopy * (ci % kCopiesPerTile) ..; lane -> row lane / kPitch, 16-byte
-  // chunk lane % kPitch of the row, read in memory order and written to its
-  // swizzled LDS slot.  Wave 0 also moves the statistics.  Each step's data
-  // is loaded into registers two steps before it is written to LDS, so that
-  // its loads have that long to land.
+  // kRowsPerCopy * (ci % kCopiesPerTile) ..; lane -> row lane / kPitch.
+  // Staged, the lane reads chunk lane % kPitch of its row in memory order and
+  // writes it to the chunk's swizzled slot; copied directly, the lane fills
+  // slot lane % kPitch and fetches the chunk that the swizzle puts there.
+  // Wave 0 also moves the statistics.
   const int ci0 = S::kCopiesPerWave * wave;
   const bool cp_q = ci0 < S::kCopiesPerTile;
   const int cp_row0 = S::kRowsPerCopy * (ci0 % S::kCopiesPerTile);
-  const int cp_c = lane % S::kPitch;                // chunk of the row in memory
-  const bool cp_on = S::kChunks == S::kPitch || cp_c < S::kChunks;  // padding chunks (head_dim 80) load nothing
-  int cp_row[S::kCopiesPerWave];        // tile row of the lane
-  uint32_t cp_dst[S::kCopiesPerWave];   // LDS byte offset of the lane's slot within the stage
+  const int cp_c = lane % S::kPitch;  // staged: chunk of the row in memory; direct: LDS slot
+  int cp_row[S::kCopiesPerWave];      // tile row of the lane
+  int cp_chunk[S::kCopiesPerWave];    // chunk of the row the lane reads
+  uint32_t cp_dst[S::kCopiesPerWave];  // staged: LDS byte offset of the lane's slot within the stage
 #pragma unroll
   for (int j = 0; j < S::kCopiesPerWave; ++j) {
     const int r = cp_row0 + S::kRowsPerCopy * j + lane / S::kPitch;
     cp_row[j] = r;
+    cp_chunk[j] = S::kStaged ? cp_c : cp_c ^ bwd_swz<S::kPitch>(r);
     cp_dst[j] = (cp_q ? 0 : S::kTileBytes) + r * S::kRowBytes + 16 * (cp_c ^ bwd_swz<S::kPitch>(r));
   }
   const int64_t cp_st = cp_q ? p.q_st : p.do_st;
   const int64_t cp_sh = cp_q ? p.q_sh : p.do_sh;
+  const uint32_t cp_row_bytes = (uint32_t)(2 * cp_st);  // direct copies: < 2^27, token strides are validated
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
   // Step st is query head hg = st % group of query tile n_qt - 1 - st / group.
-  // The loads and the compute visit the steps in order, so each keeps a
+  // The copies and the compute visit the steps in order, so each keeps a
   // cursor (head within the group, query tile, source rows) advanced one step
   // at a time instead of dividing by the runtime group size and multiplying
   // out the strides.
-  int iss_hg = 0, iss_qt = n_qt - 1;  // next step to load
+  int iss_hg = 0, iss_qt = n_qt - 1;  // next step to copy
   const uint16_t* iss_src = (cp_q ? reinterpret_cast<const uint16_t*>(p.q) + b * p.q_sb
                                   : reinterpret_cast<const uint16_t*>(p.dout) + b * p.do_sb) +
                             (int64_t)(hk * p.group) * cp_sh + (int64_t)(iss_qt * kBwdRows) * cp_st;
   const int64_t iss_wrap = (int64_t)p.group * cp_sh + kBwdRows * cp_st;
   const float* iss_stat = p.stats + 2 * (((int64_t)b * p.Hq + hk * p.group) * p.Lq + iss_qt * kBwdRows);
   const int64_t stat_sh = 2 * (int64_t)p.Lq, stat_wrap = 2 * ((int64_t)p.group * p.Lq + kBwdRows);
-  struct Staged {
-    u32x4 v[S::kCopiesPerWave];
-    float st;
-  };
-  auto load_step = [&](Staged& x) __attribute__((always_inline)) {
-    const int r0 = iss_qt * kBwdRows;
-    const uint16_t* src = iss_src;
-    const float* st_src = iss_stat;
+  auto advance = [&]() __attribute__((always_inline)) {
     iss_src += cp_sh;
     iss_stat += stat_sh;
     if (++iss_hg == p.group) {
@@ -269,15 +272,68 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
       iss_src -= iss_wrap;
       iss_stat -= stat_wrap;
     }
+  };
+
+  // Direct copies of the next step into buffer iss_buf.
+  int iss_buf = 0;
+  auto issue_step = [&]() __attribute__((always_inline)) {
+    const uint32_t stage = lds0 + iss_buf * S::kStageBytes;
+    iss_buf = iss_buf == S::kStages - 1 ? 0 : iss_buf + 1;
+    const int r0 = iss_qt * kBwdRows;
+    const uint16_t* src = iss_src;
+    const float* st_src = iss_stat;
+    advance();
+    const uint32_t dst = stage + (cp_q ? 0 : S::kTileBytes);
 #pragma unroll
     for (int j = 0; j < S::kCopiesPerWave; ++j) {
       const int row = min(r0 + cp_row[j], p.Lq - 1) - r0;  // rows past Lq repeat the last one
-      x.v[j] = cp_on ? load16(src + (int64_t)row * cp_st + 8 * cp_c) : zero16();
+      if (S::kChunks == S::kPitch || cp_chunk[j] < S::kChunks)  // slots of padding chunks (head_dim 80) stay idle
+        lds_copy16(src, (uint32_t)row * cp_row_bytes + 16u * (uint32_t)cp_chunk[j],
+                   dst + (cp_row0 + S::kRowsPerCopy * j) * S::kRowBytes);
     }
     if (wave == 0) {
       const int row = min(r0 + (lane >> 1), p.Lq - 1) - r0;
-      x.st = st_src[2 * row + (lane & 1)];
+      lds_copy4(st_src, (uint32_t)(8 * row + 4 * (lane & 1)), stage + 2 * S::kTileBytes);
     }
+  };
+  // Direct copies: waits until at most `pending` later steps' copies of this
+  // wave are in flight.
+  auto wait_steps = [&](int pending) __attribute__((always_inline)) {
+    if (wave == 0) {
+      constexpr int n = S::kCopiesPerWave + 1;
+      if (pending >= 2) __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * n));
+      else if (pending == 1) __builtin_amdgcn_s_waitcnt(0x0f70 | n);
+      else __builtin_amdgcn_s_waitcnt(0x0f70);
+    } else {
+      constexpr int n = S::kCopiesPerWave;
+      if (pending >= 2) __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * n));
+      else if (pending == 1) __builtin_amdgcn_s_waitcnt(0x0f70 | n);
+      else __builtin_amdgcn_s_waitcnt(0x0f70);
+    }
+  };
+
+  // Staged copies.  Every wave issues the same loads on every call, the
+  // statistics included (only wave 0 writes them), and calls past the last
+  // step repeat it, so that the compiler's wait before each write counts
+  // exactly the loads of the other register set.
+  struct Staged {
+    u32x4 v[S::kStaged ? S::kCopiesPerWave : 1];
+    float st;
+  };
+  int iss_n = 0;  // steps loaded so far
+  auto load_step = [&](Staged& x) __attribute__((always_inline)) {
+    const int r0 = iss_qt * kBwdRows;
+    const uint16_t* src = iss_src;
+    const float* st_src = iss_stat;
+    if (++iss_n < n_steps) advance();
+#pragma unroll
+    for (int j = 0; j < S::kCopiesPerWave; ++j) {
+      const int row = min(r0 + cp_row[j], p.Lq - 1) - r0;  // rows past Lq repeat the last one
+      // padding chunks (head_dim 80) load nothing
+      x.v[j] = S::kChunks == S::kPitch || cp_c < S::kChunks ? load16(src + (int64_t)row * cp_st + 8 * cp_c) : zero16();
+    }
+    const int row = min(r0 + (lane >> 1), p.Lq - 1) - r0;
+    x.st = st_src[2 * row + (lane & 1)];
   };
   auto write_step = [&](const Staged& x, int buf) __attribute__((always_inline)) {
     lds_char* stage = lds + buf * S::kStageBytes;
@@ -368,18 +424,26 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
     return r0 + kBwdRows <= p.Lq && wave_k0 + 32 <= p.Lk && (!CAUSAL || r0 >= wave_k0 + 31);
   };
 
-  // Steps 0 and 1 go straight to LDS; 2 and 3 wait in registers.
-  Staged stg_a{}, stg_b{};
-  if (n_steps > 0) {
-    load_step(stg_a);
-    write_step(stg_a, 0);
+  Staged stg_a, stg_b;
+  if constexpr (S::kStaged) {
+    // Steps 0 and 1 go straight to LDS; 2 and 3 wait in registers.
+    if (n_steps > 0) {
+      load_step(stg_a);
+      write_step(stg_a, 0);
+      load_step(stg_a);
+      write_step(stg_a, 1);
+      load_step(stg_a);
+      // Keep step 3's loads after step 2's: the waits in the loop count on
+      // that order (the scheduler may otherwise swap the two groups).
+      __builtin_amdgcn_sched_barrier(0);
+      load_step(stg_b);
+    }
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): K and V have landed before the copies start
+#pragma unroll
+    for (int st = 0; st < S::kAhead; ++st)
+      if (st < n_steps) issue_step();
   }
-  if (n_steps > 1) {
-    load_step(stg_a);
-    write_step(stg_a, 1);
-  }
-  if (n_steps > 2) load_step(stg_a);
-  if (n_steps > 3) load_step(stg_b);
 
   // P exchange (two roles): slot (step & 1) of this key group, lane-major
   // 16-byte chunks, chunk j of lane l at 16 (64 j + l).
@@ -403,16 +467,86 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
     grad_product(stage, dsb, 0, 0, S::kND);
   };
 
+  // A single wave's step: S = Q K^T and dP = dO V^T (their accumulation
+  // chains interleaved), P and dS packed as the B operands of the two
+  // 16-query slices, then dV^T += dO^T P and dK^T += Q^T dS block by block.
+  auto single_step = [&](int buf, int r0) __attribute__((always_inline)) {
+    const lds_char* stage = lds + buf * S::kStageBytes;
+    const lds_char* qt_l = stage;
+    const lds_char* dt_l = stage + S::kTileBytes;
+    const float* st_l = (const float*)(stage + 2 * S::kTileBytes);
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < S::kKC; ++kc) {
+      const u32x4 qa = *reinterpret_cast<const lds_u32x4*>(qt_l + (rd_off ^ (32 * kc)));
+      const u32x4 da = *reinterpret_cast<const lds_u32x4*>(dt_l + (rd_off ^ (32 * kc)));
+      s = mfma32(qa, kop[kc], s);
+      dp = mfma32(da, vop[kc], dp);
+    }
+    u32x4 pb[2], dsb[2];
+    auto scores = [&](auto mask_tag) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+      for (int cs = 0; cs < 2; ++cs) {
+        float pe[8], de[8];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          // rows rb .. rb + 3: (LSE log2 e, D) pairs of 4 consecutive rows
+          const int rb = 8 * (2 * cs + jj) + 4 * g;
+          const f32x4 s01 = *reinterpret_cast<const lds_f32x4*>((const lds_char*)st_l + 8 * rb);
+          const f32x4 s23 = *reinterpret_cast<const lds_f32x4*>((const lds_char*)st_l + 8 * rb + 16);
+          const float l2v[4] = {s01[0], s01[2], s23[0], s23[2]};
+          const float dlv[4] = {s01[1], s01[3], s23[1], s23[3]};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 8 * cs + 4 * jj + e;
+            const int qrow = r0 + rb + e;
+            const bool vis = !MASK || (qrow < p.Lq && key < p.Lk && (!CAUSAL || key <= qrow));
+            const float pv = vis ? fast_exp2(__builtin_fmaf(s[r], c, -l2v[e])) : 0.f;
+            pe[4 * jj + e] = pv;
+            de[4 * jj + e] = pv * (dp[r] - dlv[e]);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          pb[cs][j] = pack_bf16x2(pe[2 * j], pe[2 * j + 1]);
+          dsb[cs][j] = pack_bf16x2(de[2 * j], de[2 * j + 1]);
+        }
+      }
+    };
+    if (all_visible(r0))
+      scores(std::false_type{});
+    else
+      scores(std::true_type{});
+#pragma unroll
+    for (int i = 0; i < S::kND; ++i)
+#pragma unroll
+      for (int cs = 0; cs < 2; ++cs) {
+        acc[i] = mfma32(tr_read(dt_l, i, cs), pb[cs], acc[i]);
+        acc[S::kND + i] = mfma32(tr_read(qt_l, i, cs), dsb[cs], acc[S::kND + i]);
+      }
+  };
+
   int cmp_hg = 0, cmp_qt = n_qt - 1, cmp_buf = 0;  // this step's cursor
-  for (int step = 0; step < n_steps; ++step) {
+  // One step; `stg` holds step + 2 (even steps stg_a, odd steps stg_b, so
+  // that no register copy waits for loads still in flight).
+  auto run_step = [&](int step, Staged& stg) __attribute__((always_inline)) {
     const int buf = cmp_buf;
     cmp_buf = cmp_buf == S::kStages - 1 ? 0 : cmp_buf + 1;
-    __syncthreads();  // step's tiles in LDS; every wave is done with the buffer refilled next
-    // Step + 2 from registers into its buffer (free since step - 2), then the
-    // loads of step + 4.
-    if (step + 2 < n_steps) write_step(stg_a, buf + 2 < S::kStages ? buf + 2 : buf + 2 - S::kStages);
-    stg_a = stg_b;
-    if (step + 4 < n_steps) load_step(stg_b);
+    if constexpr (S::kStaged) {
+      lds_barrier();  // step's tiles in LDS; every wave is done with the buffer refilled next
+      // Step + 2 from registers into its buffer (free since step - 2), then
+      // the loads of step + 4 into the same registers.  Past the last step
+      // both move a repeat of it into a buffer no later step reads.
+      write_step(stg, buf + 2 < S::kStages ? buf + 2 : buf + 2 - S::kStages);
+      load_step(stg);
+    } else {
+      wait_steps(min(S::kAhead - 1, n_steps - 1 - step));
+      lds_barrier();  // step's tiles in LDS; every wave is done with the buffer refilled next
+      if (step + S::kAhead < n_steps) issue_step();
+    }
     if (ds_wave && prev_buf >= 0) finish_prev((step - 1) & 1);
     prev_buf = -1;
     const int qt = cmp_qt;
@@ -423,10 +557,12 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
     const int r0 = qt * kBwdRows;
     // A wave whose keys all come after the tile's last query has nothing here.
     if (!CAUSAL || r0 + kBwdRows - 1 >= wave_k0) {
-      if (ds_wave) {
+      if (!S::kRoles) {
+        single_step(buf, r0);
+      } else if (ds_wave) {
         prev_buf = buf;
       } else {
-        // P wave, or a single wave.
+        // P wave.
         const lds_char* stage = lds + buf * S::kStageBytes;
         const lds_char* qt_l = stage;
         const lds_char* dt_l = stage + S::kTileBytes;
@@ -435,27 +571,24 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
             all_visible(r0) ? probs(s, stage, r0, std::false_type{}) : probs(s, stage, r0, std::true_type{});
         u32x4 pb[2];
         pack_b(pe, pb);
-        if constexpr (S::kRoles) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<lds_f32x4*>(xchg + (step & 1) * S::kPBytes + 16 * (64 * j + lane)) =
-                f32x4{pe[4 * j], pe[4 * j + 1], pe[4 * j + 2], pe[4 * j + 3]};
-          grad_product(dt_l, pb, 0, 0, S::kND);
-        } else {
-          const f32x16 dp = row_product(dt_l, vop);
-          f32x16 ds;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) ds[r] = pe[r] * (dp[r] - row_stats(stage, r, 1));
-          u32x4 dsb[2];
-          pack_b(ds, dsb);
-          grad_product(dt_l, pb, 0, 0, S::kND);
-          grad_product(qt_l, dsb, S::kND, 0, S::kND);
-        }
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<lds_f32x4*>(xchg + (step & 1) * S::kPBytes + 16 * (64 * j + lane)) =
+              f32x4{pe[4 * j], pe[4 * j + 1], pe[4 * j + 2], pe[4 * j + 3]};
+        grad_product(dt_l, pb, 0, 0, S::kND);
       }
     }
+  };
+  // Whole pairs in the loop (so that the compiler sees both register sets
+  // loaded on every way round it), an odd last step after.
+  int step = 0;
+  for (; step + 1 < n_steps; step += 2) {
+    run_step(step, stg_a);
+    run_step(step + 1, stg_b);
   }
+  if (step < n_steps) run_step(step, stg_a);
   if constexpr (S::kRoles) {
-    __syncthreads();  // the last step's P is in LDS
+    lds_barrier();  // the last step's P is in LDS
     if (ds_wave && prev_buf >= 0) finish_prev((n_steps - 1) & 1);
   }
 

@@ -101,6 +101,17 @@ __device__ __forceinline__ void lds_copy4(const void* base, uint32_t off, uint32
   asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_base) : "memory");
 }
 
+// Workgroup barrier that orders LDS only: each wave's LDS accesses complete
+// before it, nothing else.  __syncthreads() also waits for every global load
+// the wave has in flight (its fence covers global memory), which would drain
+// loads issued to stage later tiles through registers; the kernels here share
+// data within a workgroup only through LDS.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // s_waitcnt immediate that waits until at most n vector memory operations
 // are outstanding (vmcnt(n), n < 64: bits 3:0 and 15:14) and leaves the
 // other counters unconstrained (expcnt 7, lgkmcnt 15).
