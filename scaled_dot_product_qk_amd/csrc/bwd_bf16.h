@@ -19,7 +19,7 @@
 //     forming P and dV, the other dS and dK;
 //   * attn_bwd_dq_kernel: one workgroup per (batch, query head, 128 queries);
 //     each wave keeps its 32 queries' Q, dO, LSE and D in registers and walks
-//     32-key tiles of K and V copied straight into LDS.
+//     32-key tiles of K and V staged through registers into LDS.
 // Both products of a tile that contract over its rows (dV^T += dO^T P,
 // dK^T += Q^T dS, dQ^T += K^T dS^T) take their A operand from the transposing
 // LDS read ds_read_b64_tr_b16 on the row-major tile, visiting the rows in the
@@ -105,9 +105,9 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- dK, dV
-// Largest K, V token stride (elements) the dQ kernel's copies allow: a lane's
-// 32-bit offset spans up to 31 rows of one 32-row tile.  (Q and dO are held
-// to the same bound.)
+// Largest Q, dO token stride (elements) the direct copies of the
+// single-wave dK/dV kernels allow: a lane's 32-bit offset spans up to 31 rows
+// of one 32-row tile.  (K and V are held to the same bound.)
 constexpr int64_t kBwdMaxTokenStride = int64_t(1) << 26;
 
 // dK/dV workgroup: 128 keys in 4 groups of 32.  Below head_dim 128 one wave
@@ -616,8 +616,8 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
 
 // ---------------------------------------------------------------- dQ
 // dQ workgroup: 4 waves x 32 queries of one (batch, query head); 32-key tiles
-// of K and V copied straight into LDS (the dK/dV kernel's swizzle: K is read
-// by rows and transposed), four steps in flight.
+// of K and V staged through registers into LDS (the dK/dV kernel's swizzle:
+// K is read by rows and transposed), three steps ahead of their use.
 template <int D>
 struct BwdQShape {
   static constexpr int kWaves = 4;
@@ -635,7 +635,6 @@ struct BwdQShape {
   static constexpr int kCopiesPerWave = 2 * kCopiesPerTile / kWaves;
   static_assert(kCopiesPerWave * kWaves == 2 * kCopiesPerTile, "copies split evenly over the waves");
   static_assert(kCopiesPerTile % kCopiesPerWave == 0, "a wave copies from one tile only");
-  static_assert(2 * kCopiesPerWave < 16, "the wait counts fit the simple vmcnt encoding");
   static_assert(kChunks <= kPitch, "rows fit their pitch");
 };
 
@@ -692,42 +691,41 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   int n_kt = (p.Lk + kBwdRows - 1) / kBwdRows;
   if (CAUSAL) n_kt = min(n_kt, (q0 + 127) / kBwdRows + 1);
 
-  // ---- copy plan: waves 0-1 copy the K tile, waves 2-3 the V tile ----
+  // ---- copy plan: waves 0-1 move the K tile, waves 2-3 the V tile; lane ->
+  // row lane / kPitch, 16-byte chunk lane % kPitch of the row, read in memory
+  // order and written to its swizzled LDS slot.  A tile is loaded into
+  // registers one step before it is written to LDS, three steps ahead of its
+  // use; loads past the last tile repeat it. ----
   const int ci0 = S::kCopiesPerWave * wave;
   const bool cp_k = ci0 < S::kCopiesPerTile;
   const int cp_row0 = S::kRowsPerCopy * (ci0 % S::kCopiesPerTile);
-  uint32_t cp_rel[S::kCopiesPerWave];
+  const int cp_c = lane % S::kPitch;
   int cp_row[S::kCopiesPerWave];
-  int cp_lc[S::kCopiesPerWave];
+  uint32_t cp_dst[S::kCopiesPerWave];
 #pragma unroll
   for (int j = 0; j < S::kCopiesPerWave; ++j) {
     const int r = cp_row0 + S::kRowsPerCopy * j + lane / S::kPitch;
     cp_row[j] = r;
-    cp_lc[j] = (lane % S::kPitch) ^ bwd_swz<S::kPitch>(r);  // logical chunk of the lane's slot
-    cp_rel[j] = 16u * (uint32_t)cp_lc[j];
+    cp_dst[j] = (cp_k ? 0 : S::kTileBytes) + r * S::kRowBytes + 16 * (cp_c ^ bwd_swz<S::kPitch>(r));
   }
   const int64_t cp_st = cp_k ? p.k_st : p.v_st;
-  const uint32_t cp_row_bytes = (uint32_t)(2 * cp_st);  // < 2^27: token strides are validated
   const uint16_t* cp_base = cp_k ? reinterpret_cast<const uint16_t*>(p.k) + b * p.k_sb + hk * p.k_sh
                                  : reinterpret_cast<const uint16_t*>(p.v) + b * p.v_sb + hk * p.v_sh;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-  auto issue_step = [&](int t) {
-    const int r0 = t * kBwdRows;
-    const uint32_t dst = lds0 + (t % S::kStages) * S::kStageBytes + (cp_k ? 0 : S::kTileBytes);
-    const uint16_t* src = cp_base + (int64_t)r0 * cp_st;
+  u32x4 stg[S::kCopiesPerWave];
+  auto load_tile = [&](int t) __attribute__((always_inline)) {
+    const int r0 = min(t, n_kt - 1) * kBwdRows;
+    const uint16_t* src = cp_base + (int64_t)r0 * cp_st + 8 * cp_c;
 #pragma unroll
     for (int j = 0; j < S::kCopiesPerWave; ++j) {
       const int row = min(r0 + cp_row[j], p.Lk - 1) - r0;  // keys past Lk repeat the last one
-      if (S::kChunks == S::kPitch || cp_lc[j] < S::kChunks)
-        lds_copy16(src, (uint32_t)row * cp_row_bytes + cp_rel[j],
-                   dst + (cp_row0 + S::kRowsPerCopy * j) * S::kRowBytes);
+      stg[j] = S::kChunks == S::kPitch || cp_c < S::kChunks ? load16(src + (int64_t)row * cp_st) : zero16();
     }
   };
-  auto wait_steps = [&](int pending) {
-    constexpr int n = S::kCopiesPerWave;
-    if (pending >= 2) __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * n));
-    else if (pending == 1) __builtin_amdgcn_s_waitcnt(0x0f70 | n);
-    else __builtin_amdgcn_s_waitcnt(0x0f70);
+  auto write_tile = [&](int buf) __attribute__((always_inline)) {
+    lds_char* stage = lds + buf * S::kStageBytes;
+#pragma unroll
+    for (int j = 0; j < S::kCopiesPerWave; ++j)
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(stage + cp_dst[j]) = stg[j];
   };
 
   const int rd_off = ln * S::kRowBytes + 16 * (g ^ bwd_swz<S::kPitch>(ln));
@@ -741,15 +739,22 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
     }
   }
 
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): Q, dO and the statistics have landed
+  // Tiles 0-2 go straight to LDS; tile 3 waits in registers.
+  if (n_kt > 0) {
 #pragma unroll
-  for (int t = 0; t < S::kStages - 1; ++t)
-    if (t < n_kt) issue_step(t);
+    for (int t = 0; t < S::kStages - 1; ++t) {
+      load_tile(t);
+      write_tile(t);
+    }
+    load_tile(S::kStages - 1);
+  }
 
   for (int t = 0; t < n_kt; ++t) {
-    wait_steps(min(S::kStages - 2, n_kt - 1 - t));
-    __syncthreads();
-    if (t + S::kStages - 1 < n_kt) issue_step(t + S::kStages - 1);
+    lds_barrier();  // tile t in LDS; every wave is done with tile t - 1's buffer
+    // Tile t + 3 from registers into tile t - 1's buffer, then the loads of
+    // t + 4 (past the last tile, repeats of it into buffers no later step reads).
+    write_tile((t + S::kStages - 1) % S::kStages);
+    load_tile(t + S::kStages);
     const int kv0 = t * kBwdRows;
     if (!CAUSAL || kv0 <= wave_q0 + 31) {
       const lds_char* kt_l = lds + (t % S::kStages) * S::kStageBytes;
