@@ -340,7 +340,8 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
 #pragma unroll
     for (int j = 0; j < S::kCopiesPerWave; ++j) *reinterpret_cast<lds_u32x4*>(stage + cp_dst[j]) = x.v[j];
     if (wave == 0)
-      *reinterpret_cast<__attribute__((address_space(3))) float*>(stage + 2 * S::kTileBytes + 4 * lane) = x.st;
+      *reinterpret_cast<__attribute__((address_space(3))) float*>(
+          stage + 2 * S::kTileBytes + 4 * (32 * (lane & 1) + (lane >> 1))) = x.st;  // all LSE, then all D
   };
 
   // ---- LDS operand offsets within a tile ----
@@ -384,9 +385,11 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
   };
   // Statistics of the rows this lane's accumulator registers hold: row
   // 8 (r / 4) + 4 g + r % 4 of the tile; element 0 is LSE log2 e, 1 is D.
+  // (Staged tiles, the two-role kernel: the tile's 32 LSE values, then its
+  // 32 D values, so that a role reads its 16 with four 16-byte reads.)
   auto row_stats = [&](const lds_char* stage, int r, int e) __attribute__((always_inline)) {
     return *reinterpret_cast<const __attribute__((address_space(3))) float*>(
-        stage + 2 * S::kTileBytes + 8 * (8 * (r >> 2) + 4 * g + (r & 3)) + 4 * e);
+        stage + 2 * S::kTileBytes + 4 * (32 * e + 8 * (r >> 2) + 4 * g + (r & 3)));
   };
   // P = exp2(c S - LSE log2 e), zero for pairs that do not take part (rows
   // past Lq, keys past Lk, causal keys after the query).
