@@ -4,6 +4,7 @@
 // allocation, no state, no fallback: anything without a kernel is an error.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <limits>
@@ -452,7 +453,21 @@ static attn_status_t launch_bwd_dkdv(const BwdParams& p, int grid, hipStream_t s
       return ATTN_ERR_HIP;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * S::kWaves), S::kLdsBytes, s, p);
+  // Key blocks per (batch, kv head) that are resident from the start: the
+  // grid's first (compute units x workgroups per unit) blocks, key block
+  // slowest.  Causal, the later ones walk their query tiles upward.
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)kern, 64 * S::kWaves, S::kLdsBytes) !=
+            hipSuccess ||
+        n <= 0)
+      n = 1;
+    per_cu = n;
+  }
+  BwdParams q = p;
+  q.kv_round1 = (int)((int64_t)device_cu_count() * per_cu / std::max(1, p.B * p.Hkv));
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * S::kWaves), S::kLdsBytes, s, q);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -519,6 +534,7 @@ extern "C" attn_status_t attn_bwd(const attn_bwd_args_t* a, void* workspace, siz
   p.group = (int)(a->Hq / a->Hkv);
   p.Lq = (int)a->Lq;
   p.Lk = (int)a->Lk;
+  p.kv_round1 = 0;  // set per launch of the dK/dV kernel
   p.scale = effective_scale(a->scale, a->d);
   p.scale_log2 = p.scale * kLog2e;
   const bool c = a->causal != 0;

@@ -60,6 +60,7 @@ struct BwdParams {
   int64_t dk_sb, dk_sh, dk_st;
   int64_t dv_sb, dv_sh, dv_st;
   int B, Hq, Hkv, group, Lq, Lk;
+  int kv_round1;     // dK/dV: key blocks per (batch, kv head) resident from the start (causal step order)
   float scale;       // softmax scale (signed)
   float scale_log2;  // scale * log2(e)
 };
@@ -218,12 +219,20 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-  // Steps: query tiles from the last down to the first one with a query at
-  // or after k0 (causal), the group's query heads within each tile, so that
-  // all key blocks of a kv head walk the same tiles at the same time.
+  // Steps: the query tiles from the first one with a query at or after k0
+  // (causal) to the last, the group's query heads within each tile, so that
+  // the key blocks of a kv head running together walk the same tiles at the
+  // same time and share them through L2.  The key blocks resident from the
+  // start walk the tiles from the last down: they all start on the same one.
+  // Causal, a later key block starts when an earlier (heavier) one ends, at
+  // a time that grows with its index by as much as its own number of tiles
+  // shrinks; walking up from its diagonal, each is on tile `time - const`
+  // like the others.
   const int n_qt = (p.Lq + kBwdRows - 1) / kBwdRows;
   const int qt_lo = CAUSAL ? min(k0 / kBwdRows, n_qt) : 0;
   const int n_steps = p.group * (n_qt - qt_lo);
+  const bool ascend = CAUSAL && kb >= p.kv_round1;
+  const int qt_first = ascend ? qt_lo : n_qt - 1, qt_dir = ascend ? 1 : -1;
   const float c = p.scale_log2;
 
   // ---- copy plan: wave w moves chunks kCopiesPerWave * w .. +kCopiesPerWave-1
@@ -251,24 +260,24 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
   const int64_t cp_sh = cp_q ? p.q_sh : p.do_sh;
   const uint32_t cp_row_bytes = (uint32_t)(2 * cp_st);  // direct copies: < 2^27, token strides are validated
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-  // Step st is query head hg = st % group of query tile n_qt - 1 - st / group.
+  // Step st is query head hg = st % group of query tile qt_first + qt_dir * (st / group).
   // The copies and the compute visit the steps in order, so each keeps a
   // cursor (head within the group, query tile, source rows) advanced one step
   // at a time instead of dividing by the runtime group size and multiplying
   // out the strides.
-  int iss_hg = 0, iss_qt = n_qt - 1;  // next step to copy
+  int iss_hg = 0, iss_qt = qt_first;  // next step to copy
   const uint16_t* iss_src = (cp_q ? reinterpret_cast<const uint16_t*>(p.q) + b * p.q_sb
                                   : reinterpret_cast<const uint16_t*>(p.dout) + b * p.do_sb) +
                             (int64_t)(hk * p.group) * cp_sh + (int64_t)(iss_qt * kBwdRows) * cp_st;
-  const int64_t iss_wrap = (int64_t)p.group * cp_sh + kBwdRows * cp_st;
+  const int64_t iss_wrap = (int64_t)p.group * cp_sh - qt_dir * kBwdRows * cp_st;
   const float* iss_stat = p.stats + 2 * (((int64_t)b * p.Hq + hk * p.group) * p.Lq + iss_qt * kBwdRows);
-  const int64_t stat_sh = 2 * (int64_t)p.Lq, stat_wrap = 2 * ((int64_t)p.group * p.Lq + kBwdRows);
+  const int64_t stat_sh = 2 * (int64_t)p.Lq, stat_wrap = 2 * ((int64_t)p.group * p.Lq - qt_dir * kBwdRows);
   auto advance = [&]() __attribute__((always_inline)) {
     iss_src += cp_sh;
     iss_stat += stat_sh;
     if (++iss_hg == p.group) {
       iss_hg = 0;
-      --iss_qt;
+      iss_qt += qt_dir;
       iss_src -= iss_wrap;
       iss_stat -= stat_wrap;
     }
@@ -532,7 +541,7 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
       }
   };
 
-  int cmp_hg = 0, cmp_qt = n_qt - 1, cmp_buf = 0;  // this step's cursor
+  int cmp_hg = 0, cmp_qt = qt_first, cmp_buf = 0;  // this step's cursor
   // One step; `stg` holds step + 2 (even steps stg_a, odd steps stg_b, so
   // that no register copy waits for loads still in flight).
   auto run_step = [&](int step, Staged& stg) __attribute__((always_inline)) {
@@ -555,7 +564,7 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
     const int qt = cmp_qt;
     if (++cmp_hg == p.group) {
       cmp_hg = 0;
-      --cmp_qt;
+      cmp_qt += qt_dir;
     }
     const int r0 = qt * kBwdRows;
     // A wave whose keys all come after the tile's last query has nothing here.
