@@ -94,6 +94,23 @@ def test_bwd_small(dev, d, causal, shape):
     grad_check("dv", to_np(dv), rv, label)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_causal_key_blocks_walking_up(dev, d):
+    """Causal, with as many (batch, kv head) pairs as compute units: only the
+    first one or two key blocks of each pair are resident from the start,
+    and the later ones walk their query tiles upward from their diagonal.
+    Full comparison, n = 360 (the last key block ragged)."""
+    B, Hq, Hkv, L = 16, 32, 16, 360
+    w = wl.FwdWorkload("bwd_up", B, Hq, Hkv, L, L, d, "bf16", True, 990 + d)
+    q, k, v, do = inputs(w, 991 + d)
+    dq, dk, dv = run_gpu(q, k, v, do, dev, True)
+    rq, rk, rv = orc.attention_backward(q, k, v, do, causal=True)
+    label = f"bwd walking up d{d}"
+    grad_check("dq", to_np(dq), rq, label)
+    grad_check("dk", to_np(dk), rk, label)
+    grad_check("dv", to_np(dv), rv, label)
+
+
 def test_bwd_deterministic(dev):
     w = wl.FwdWorkload("bwd_det", 1, 8, 2, 700, 700, 128, "bf16", True, 960)
     q, k, v, do = inputs(w, 961)
