@@ -118,10 +118,8 @@ constexpr int64_t kBwdMaxTokenStride = int64_t(1) << 26;
 // P, hands P to its partner through LDS and accumulates dV; the dS wave
 // forms dP = dO V^T, and after the next barrier takes P, forms dS and
 // accumulates dK.  Each product is formed once, and the two waves of a group
-// have the same matrix work per step.  Q and dO tiles of 32 rows and the
-// rows' (LSE log2 e, D) pairs are loaded into registers and written to LDS
-// two steps ahead of the one computed (direct global-to-LDS copies made this
-// kernel about a fifth slower).
+// have the same matrix work per step.  Each step moves a 32-row Q tile, a
+// 32-row dO tile and the rows' (LSE log2 e, D) pairs into LDS (below).
 template <int D>
 struct BwdKvShape {
   static constexpr bool kRoles = D == 128;
@@ -542,8 +540,9 @@ __global__ __launch_bounds__(64 * BwdKvShape<D>::kWaves, 1) void attn_bwd_dkdv_k
   };
 
   int cmp_hg = 0, cmp_qt = qt_first, cmp_buf = 0;  // this step's cursor
-  // One step; `stg` holds step + 2 (even steps stg_a, odd steps stg_b, so
-  // that no register copy waits for loads still in flight).
+  // One step.  Staged, `stg` holds step + 2 (even steps stg_a, odd steps
+  // stg_b, so that no register copy waits for loads still in flight);
+  // copying directly, it is unused.
   auto run_step = [&](int step, Staged& stg) __attribute__((always_inline)) {
     const int buf = cmp_buf;
     cmp_buf = cmp_buf == S::kStages - 1 ? 0 : cmp_buf + 1;
