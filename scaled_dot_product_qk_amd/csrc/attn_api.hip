@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <limits>
@@ -51,16 +52,16 @@ int64_t decode_pieces(int64_t Lmax) { return Lmax > 0 ? (Lmax - 1) / kDecMinPiec
 
 // Compute units of the current device (queried once per device).
 int device_cu_count() {
-  static int counts[64] = {0};
+  static std::atomic<int> counts[64];  // zero until queried; racing first calls store the same value
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
   if (dev >= 64) dev = 63;
-  if (counts[dev] == 0) {
-    int n = 0;
+  int n = counts[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    counts[dev] = n;
+    counts[dev].store(n, std::memory_order_relaxed);
   }
-  return counts[dev];
+  return n;
 }
 
 }  // namespace
@@ -116,12 +117,12 @@ template <int D, bool CAUSAL, int MK = 0>
 static attn_status_t launch_fwd_bf16(const FwdParams& p, int grid_x, hipStream_t s) {
   constexpr int lds = FwdMaskShape<D, CAUSAL, MK>::kKernelLdsBytes;
   auto kern = attn_fwd_bf16_kernel<D, CAUSAL, MK>;
-  static bool attr_set = false;  // racing first calls set the same value
-  if (!attr_set) {
+  static std::atomic<bool> attr_set{false};  // racing first calls set the same value
+  if (!attr_set.load(std::memory_order_relaxed)) {
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=
         hipSuccess)
       return ATTN_ERR_HIP;
-    attr_set = true;
+    attr_set.store(true, std::memory_order_relaxed);
   }
   FwdParams q = p;
   q.n_qtiles = (p.Lq + Bf16FwdShape<D>::kBR - 1) / Bf16FwdShape<D>::kBR;
@@ -133,12 +134,12 @@ template <int D, bool CAUSAL>
 static attn_status_t launch_fwd_f32(const FwdParams& p, int grid_x, hipStream_t s) {
   constexpr int lds = F32FwdShape<D>::kLdsBytes;
   auto kern = attn_fwd_f32_kernel<D, CAUSAL>;
-  static bool attr_set = false;
-  if (!attr_set) {
+  static std::atomic<bool> attr_set{false};  // racing first calls set the same value
+  if (!attr_set.load(std::memory_order_relaxed)) {
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=
         hipSuccess)
       return ATTN_ERR_HIP;
-    attr_set = true;
+    attr_set.store(true, std::memory_order_relaxed);
   }
   hipLaunchKernelGGL(kern, dim3(grid_x, (p.Lq + 127) / 128), dim3(256), lds, s, p);
   return launch_status();
@@ -352,11 +353,11 @@ static attn_status_t launch_fwd_fp8(const FwdParams& p, int grid_x, hipStream_t 
   using S = Fp8FwdShape<D>;
   constexpr int lds = S::kLdsBytes;
   auto kern = attn_fwd_fp8_kernel<D, CAUSAL>;
-  static bool attr_set = false;  // racing first calls set the same value
-  if (!attr_set) {
+  static std::atomic<bool> attr_set{false};  // racing first calls set the same value
+  if (!attr_set.load(std::memory_order_relaxed)) {
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
       return ATTN_ERR_HIP;
-    attr_set = true;
+    attr_set.store(true, std::memory_order_relaxed);
   }
   FwdParams q = p;
   q.n_qtiles = (p.Lq + S::kBR - 1) / S::kBR;
@@ -446,24 +447,24 @@ template <int D, bool CAUSAL>
 static attn_status_t launch_bwd_dkdv(const BwdParams& p, int grid, hipStream_t s) {
   using S = BwdKvShape<D>;
   auto kern = attn_bwd_dkdv_kernel<D, CAUSAL>;
-  static bool attr_set = false;  // racing first calls set the same value
-  if (!attr_set) {
+  static std::atomic<bool> attr_set{false};  // racing first calls set the same value
+  if (!attr_set.load(std::memory_order_relaxed)) {
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, S::kLdsBytes) !=
         hipSuccess)
       return ATTN_ERR_HIP;
-    attr_set = true;
+    attr_set.store(true, std::memory_order_relaxed);
   }
   // Key blocks per (batch, kv head) that are resident from the start: the
   // grid's first (compute units x workgroups per unit) blocks, key block
   // slowest.  Causal, the later ones walk their query tiles upward.
-  static int per_cu = 0;
+  static std::atomic<int> per_cu_cache{0};  // racing first calls store the same value
+  int per_cu = per_cu_cache.load(std::memory_order_relaxed);
   if (per_cu == 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)kern, 64 * S::kWaves, S::kLdsBytes) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, 64 * S::kWaves, S::kLdsBytes) !=
             hipSuccess ||
-        n <= 0)
-      n = 1;
-    per_cu = n;
+        per_cu <= 0)
+      per_cu = 1;
+    per_cu_cache.store(per_cu, std::memory_order_relaxed);
   }
   BwdParams q = p;
   q.kv_round1 = (int)((int64_t)device_cu_count() * per_cu / std::max(1, p.B * p.Hkv));
@@ -475,12 +476,12 @@ template <int D, bool CAUSAL>
 static attn_status_t launch_bwd_dq(const BwdParams& p, int grid, hipStream_t s) {
   using S = BwdQShape<D>;
   auto kern = attn_bwd_dq_kernel<D, CAUSAL>;
-  static bool attr_set = false;  // racing first calls set the same value
-  if (!attr_set) {
+  static std::atomic<bool> attr_set{false};  // racing first calls set the same value
+  if (!attr_set.load(std::memory_order_relaxed)) {
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, S::kLdsBytes) !=
         hipSuccess)
       return ATTN_ERR_HIP;
-    attr_set = true;
+    attr_set.store(true, std::memory_order_relaxed);
   }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * S::kWaves), S::kLdsBytes, s, p);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
