@@ -94,18 +94,19 @@ def test_bwd_small(dev, d, causal, shape):
     grad_check("dv", to_np(dv), rv, label)
 
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_bwd_causal_key_blocks_walking_up(dev, d):
+@pytest.mark.parametrize("d,Lq,Lk", [(64, 360, 360), (80, 360, 360), (128, 360, 360), (128, 300, 420)])
+def test_bwd_causal_key_blocks_walking_up(dev, d, Lq, Lk):
     """Causal, with as many (batch, kv head) pairs as compute units: only the
     first one or two key blocks of each pair are resident from the start,
     and the later ones walk their query tiles upward from their diagonal.
-    Full comparison, n = 360 (the last key block ragged)."""
-    B, Hq, Hkv, L = 16, 32, 16, 360
-    w = wl.FwdWorkload("bwd_up", B, Hq, Hkv, L, L, d, "bf16", True, 990 + d)
-    q, k, v, do = inputs(w, 991 + d)
+    Full comparison; the last key block ragged, and one case with more keys
+    than queries."""
+    B, Hq, Hkv = 16, 32, 16
+    w = wl.FwdWorkload("bwd_up", B, Hq, Hkv, Lq, Lk, d, "bf16", True, 990 + d + Lk)
+    q, k, v, do = inputs(w, 991 + d + Lk)
     dq, dk, dv = run_gpu(q, k, v, do, dev, True)
     rq, rk, rv = orc.attention_backward(q, k, v, do, causal=True)
-    label = f"bwd walking up d{d}"
+    label = f"bwd walking up d{d} Lq={Lq} Lk={Lk}"
     grad_check("dq", to_np(dq), rq, label)
     grad_check("dk", to_np(dk), rk, label)
     grad_check("dv", to_np(dv), rv, label)
