@@ -1,7 +1,10 @@
 // Host side of the attention library: the C ABI declared in include/attn.h.
 // Validates arguments on the host, picks the kernel instance for (dtype,
 // head_dim, causal), sizes the grid and launches on the caller's stream.  No
-// allocation, no state, no fallback: anything without a kernel is an error.
+// allocation and no fallback: anything without a kernel is an error.  The
+// only state is memoised device queries (compute units, occupancy, the LDS
+// attribute set once per kernel) and the allocation-free decode entry point's
+// static scratch.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
