@@ -503,7 +503,7 @@ static attn_status_t launch_bwd(const BwdParams& p, bool causal, hipStream_t s) 
     const attn_status_t st = causal ? launch_bwd_dkdv<D, true>(p, g_kv, s) : launch_bwd_dkdv<D, false>(p, g_kv, s);
     if (st != ATTN_OK) return st;
   }
-  const int g_q = p.B * p.Hq * ((p.Lq + 127) / 128);
+  const int g_q = p.B * p.Hq * ((p.Lq + BwdQShape<D>::kRows - 1) / BwdQShape<D>::kRows);
   if (g_q > 0) {
     const attn_status_t st = causal ? launch_bwd_dq<D, true>(p, g_q, s) : launch_bwd_dq<D, false>(p, g_q, s);
     if (st != ATTN_OK) return st;
