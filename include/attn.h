@@ -330,6 +330,14 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq);
  * independent; causal or not; Q, dO, K and V token strides below 2^26 elements
  * (ATTN_ERR_UNSUPPORTED past it).  dK and dV of keys that no query sees are 0;
  * Lq == 0 gives dK = dV = 0.  B == 0, Hq == 0 or Lq == Lk == 0 is a no-op.
+ * At d = 64 and 80 the dQ kernel runs on a second stream that the library
+ * keeps per device, forked from `stream` after the row sums and joined back
+ * into it (events, no host wait) before the call returns, so that it overlaps
+ * the dK/dV kernel; all results are then ordered on `stream` as if every
+ * kernel ran there.  Concurrent calls on one device take turns (a host lock)
+ * for that sequence.  A call made while `stream` is being captured into a
+ * graph, before the library has created its stream on the device, runs all
+ * three kernels on `stream`.
  */
 attn_status_t attn_bwd(const attn_bwd_args_t *args, void *workspace, size_t workspace_bytes,
                        void *stream);

@@ -3,8 +3,9 @@
 // head_dim, causal), sizes the grid and launches on the caller's stream.  No
 // allocation and no fallback: anything without a kernel is an error.  The
 // only state is memoised device queries (compute units, occupancy, the LDS
-// attribute set once per kernel) and the allocation-free decode entry point's
-// static scratch.
+// attribute set once per kernel), one extra stream and two events per device
+// for the backward (created at its first call on the device), and the
+// allocation-free decode entry point's static scratch.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -65,6 +66,39 @@ int device_cu_count() {
     counts[dev].store(n, std::memory_order_relaxed);
   }
   return n;
+}
+
+// A second stream of the library's per device, with the two events that fork
+// it from a caller's stream and join it back.  Created at the first request
+// on the device that is not made while the caller's stream is being captured
+// into a graph (creating a stream there could end the capture); until then,
+// and if creation fails, there is none.  `m` serialises the fork / launch /
+// join sequences of concurrent callers, which share the two events.
+struct SideStream {
+  std::once_flag once;
+  std::atomic<bool> ready{false};
+  bool ok = false;
+  std::mutex m;
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
+SideStream* side_stream(hipStream_t caller) {
+  static SideStream sides[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  SideStream& x = sides[dev];
+  if (!x.ready.load(std::memory_order_acquire)) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    std::call_once(x.once, [&x] {
+      x.ok = hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) == hipSuccess &&
+             hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) == hipSuccess &&
+             hipEventCreateWithFlags(&x.join, hipEventDisableTiming) == hipSuccess;
+      x.ready.store(true, std::memory_order_release);
+    });
+  }
+  return x.ok ? &x : nullptr;
 }
 
 }  // namespace
@@ -490,6 +524,14 @@ static attn_status_t launch_bwd_dq(const BwdParams& p, int grid, hipStream_t s) 
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+// The dK/dV and dQ kernels read the inputs and the row statistics, not each
+// other's results.  At head_dim 64 and 80 a workgroup of each fits on one
+// compute unit beside the other, so the dQ kernel runs on the library's
+// second stream, forked from the caller's stream after the statistics kernel
+// and joined back into it before attn_bwd returns (events only, no host
+// wait): its workgroups take the slots the dK/dV kernel leaves idle, most of
+// all in the causal tail.  At head_dim 128 each kernel fills the compute
+// units by itself and both run on the caller's stream.
 template <int D>
 static attn_status_t launch_bwd(const BwdParams& p, bool causal, hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.Hq * p.Lq;
@@ -499,16 +541,30 @@ static attn_status_t launch_bwd(const BwdParams& p, bool causal, hipStream_t s) 
     if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
   }
   const int g_kv = p.B * p.Hkv * ((p.Lk + 127) / 128);
-  if (g_kv > 0) {
-    const attn_status_t st = causal ? launch_bwd_dkdv<D, true>(p, g_kv, s) : launch_bwd_dkdv<D, false>(p, g_kv, s);
-    if (st != ATTN_OK) return st;
-  }
   const int g_q = p.B * p.Hq * ((p.Lq + BwdQShape<D>::kRows - 1) / BwdQShape<D>::kRows);
-  if (g_q > 0) {
-    const attn_status_t st = causal ? launch_bwd_dq<D, true>(p, g_q, s) : launch_bwd_dq<D, false>(p, g_q, s);
-    if (st != ATTN_OK) return st;
+  SideStream* side = D <= 80 && g_kv > 0 && g_q > 0 ? side_stream(s) : nullptr;
+  auto dkdv = [&]() {
+    if (g_kv <= 0) return ATTN_OK;
+    return causal ? launch_bwd_dkdv<D, true>(p, g_kv, s) : launch_bwd_dkdv<D, false>(p, g_kv, s);
+  };
+  auto dq = [&](hipStream_t sq) {
+    if (g_q <= 0) return ATTN_OK;
+    return causal ? launch_bwd_dq<D, true>(p, g_q, sq) : launch_bwd_dq<D, false>(p, g_q, sq);
+  };
+  if (!side) {
+    const attn_status_t st = dkdv();
+    return st != ATTN_OK ? st : dq(s);
   }
-  return ATTN_OK;
+  std::lock_guard<std::mutex> lock(side->m);
+  if (hipEventRecord(side->fork, s) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+    return ATTN_ERR_HIP;
+  attn_status_t st = dq(side->s);
+  if (st == ATTN_OK) st = dkdv();
+  // joined even after a failed launch, so that nothing of this call runs
+  // unordered with the caller's later work
+  if (hipEventRecord(side->join, side->s) != hipSuccess || hipStreamWaitEvent(s, side->join, 0) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return st;
 }
 
 extern "C" attn_status_t attn_bwd(const attn_bwd_args_t* a, void* workspace, size_t workspace_bytes,

@@ -121,6 +121,40 @@ def test_bwd_deterministic(dev):
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("d", [64, 80, 128])
+def test_bwd_results_ordered_on_callers_stream(dev, d):
+    """At head_dim 64 and 80 the dQ kernel runs on the library's second
+    stream, forked after the row sums and joined back before attn_bwd
+    returns.  On a side stream of the caller's, the workspace and outputs are
+    poisoned with NaN right before each call and copied right after it, all
+    on that stream with no host wait in between: the copies must hold the
+    gradients of a plain call (the fork orders the row sums before dQ, the
+    join orders dQ before the copies)."""
+    w = wl.FwdWorkload("bwd_order", 1, 16, 4, 2048, 2048, d, "bf16", True, 990 + d)
+    q, k, v, do = inputs(w, 991 + d)
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    o, lse = sdpa.attn_fwd(qd, kd, vd, causal=True)
+    ref = sdpa.attn_bwd(qd, kd, vd, o, lse, dod, causal=True)
+    torch.cuda.synchronize()
+    s2 = torch.cuda.Stream(device=dev)
+    ws = torch.empty(sdpa.attn_bwd_workspace_bytes(w.B, w.Hq, w.Lq), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)]
+    copies = []
+    s2.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s2):
+        for _ in range(3):
+            ws.fill_(255)  # all-ones bytes: NaN as fp32
+            for t in outs:
+                t.fill_(float("nan"))
+            sdpa.attn_bwd(qd, kd, vd, o, lse, dod, causal=True, dq=outs[0], dk=outs[1], dv=outs[2],
+                          workspace=ws, stream=s2)
+            copies.append([t.clone() for t in outs])
+    torch.cuda.synchronize()
+    for got in copies:
+        for name, x, y in zip(("dq", "dk", "dv"), got, ref):
+            assert torch.equal(x, y), name
+
+
 def test_bwd_no_queries_gives_zero_key_gradients(dev):
     q = torch.zeros(1, 2, 0, 64, dtype=torch.bfloat16, device=dev)
     k = torch.randn(1, 2, 100, 64, device=dev).to(torch.bfloat16)
