@@ -525,13 +525,12 @@ static attn_status_t launch_bwd_dq(const BwdParams& p, int grid, hipStream_t s) 
 }
 
 // The dK/dV and dQ kernels read the inputs and the row statistics, not each
-// other's results.  At head_dim 64 and 80 a workgroup of each fits on one
-// compute unit beside the other, so the dQ kernel runs on the library's
-// second stream, forked from the caller's stream after the statistics kernel
-// and joined back into it before attn_bwd returns (events only, no host
-// wait): its workgroups take the slots the dK/dV kernel leaves idle, most of
-// all in the causal tail.  At head_dim 128 each kernel fills the compute
-// units by itself and both run on the caller's stream.
+// other's results.  At head_dim 64 and 80 the dQ kernel runs on the
+// library's second stream, forked from the caller's stream after the
+// statistics kernel and joined back into it before attn_bwd returns (events
+// only, no host wait): its workgroups take the compute units the dK/dV
+// kernel's causal tail frees (and at 64 slots beside its workgroups).  At
+// head_dim 128 that measured no gain, and both run on the caller's stream.
 template <int D>
 static attn_status_t launch_bwd(const BwdParams& p, bool causal, hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.Hq * p.Lq;
