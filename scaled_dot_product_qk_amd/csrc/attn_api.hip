@@ -87,6 +87,12 @@ SideStream* side_stream(hipStream_t caller) {
   static SideStream sides[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  // The second stream lives on the current device: a caller's stream of
+  // another device keeps all the work.
+  if (caller != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(caller, &sdev) != hipSuccess || sdev != dev) return nullptr;
+  }
   SideStream& x = sides[dev];
   if (!x.ready.load(std::memory_order_acquire)) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
