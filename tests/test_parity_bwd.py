@@ -155,6 +155,37 @@ def test_bwd_results_ordered_on_callers_stream(dev, d):
             assert torch.equal(x, y), name
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_graph_replays(dev, d):
+    """attn_bwd captured into a graph after an eager call (so that at d = 64
+    the capture holds the fork to the library's second stream and the join
+    back), replayed three times with eager work between the replays that
+    poisons the outputs and workspace: every replay must reproduce the eager
+    gradients exactly."""
+    w = wl.FwdWorkload("bwd_graph", 1, 8, 2, 1024, 1024, d, "bf16", True, 1010 + d)
+    q, k, v, do = inputs(w, 1011 + d)
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    o, lse = sdpa.attn_fwd(qd, kd, vd, causal=True)
+    ws = torch.empty(sdpa.attn_bwd_workspace_bytes(w.B, w.Hq, w.Lq), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)]
+    ref = sdpa.attn_bwd(qd, kd, vd, o, lse, dod, causal=True)
+    sdpa.attn_bwd(qd, kd, vd, o, lse, dod, causal=True, dq=outs[0], dk=outs[1], dv=outs[2], workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sdpa.attn_bwd(qd, kd, vd, o, lse, dod, causal=True, dq=outs[0], dk=outs[1], dv=outs[2], workspace=ws)
+    for _ in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        ws.fill_(255)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, x, y in zip(("dq", "dk", "dv"), outs, ref):
+            assert torch.equal(x, y), name
+        sdpa.attn_fwd(qd, kd, vd, causal=True)  # eager work between replays
+
+
 def test_bwd_no_queries_gives_zero_key_gradients(dev):
     q = torch.zeros(1, 2, 0, 64, dtype=torch.bfloat16, device=dev)
     k = torch.randn(1, 2, 100, 64, device=dev).to(torch.bfloat16)
