@@ -11,7 +11,8 @@ synchronisations.  The host-side cost of a call (argument checks, marshalling
 and the launches, no device synchronisation) is timed separately with a CPU
 clock, through the Python binding and through the bare C entry point.
 After the step loop, attn_fwd_varlen on 16 packed causal GQA sequences of
-256..4096 tokens (d=128), attn_bwd on the causal GQA n=8192 d=128 workload,
+256..4096 tokens (d=128), attn_bwd on the causal GQA n=8192 d=128 workload
+and on the same shape at d=64 (where the dQ kernel runs beside dK/dV),
 attn_fwd_masked on the n=4096 d=64 workload with one boolean mask shared by
 all heads, attn_fwd_fp8 on e4m3 versions of the two prefill workloads,
 attn_fwd on the causal B=4, H=16, n=2048, d=80 workload (the head size that
@@ -88,7 +89,8 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--only", choices=["all", "fwd_n4096", "fwd_causal_n8192", "decode", "fwd_varlen", "bwd", "fwd_scaling",
+    ap.add_argument("--only", choices=["all", "fwd_n4096", "fwd_causal_n8192", "decode", "fwd_varlen", "bwd", "bwd_d64",
+                                       "fwd_scaling",
                                        "fwd_masked", "fwd_fp8_n4096", "fwd_fp8_causal_n8192", "fwd_c3_d80"],
                     default="all",
                     help="time one call of the step only (profiling runs)")
@@ -235,7 +237,7 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
 
-    SOLO = ("fwd_c3_d80", "fwd_varlen", "bwd", "fwd_masked", "fwd_fp8_n4096", "fwd_fp8_causal_n8192",
+    SOLO = ("fwd_c3_d80", "fwd_varlen", "bwd", "bwd_d64", "fwd_masked", "fwd_fp8_n4096", "fwd_fp8_causal_n8192",
             "fwd_scaling_2048", "fwd_scaling_4096", "fwd_scaling_8192")
     names = ["fwd_n4096", "fwd_causal_n8192", "decode"] if args.only == "all" else \
         ([] if args.only in SOLO or args.only == "fwd_scaling" else [args.only])
@@ -298,6 +300,18 @@ def main():
         om = torch.empty_like(GM[0])
         lm = torch.empty(GM[0].shape[:3], dtype=torch.float32, device=dev)
         calls["fwd_masked"] = lambda: sdpa.attn_fwd_masked(*GM, mm, out=om, lse=lm, stream=stream)
+    C4D64 = wl.shrink(wl.C4, name="fwd_bf16_causal_gqa_b1_hq32_hkv8_n8192_d64", d=64)
+    if "bwd_d64" in solo:
+        q6, k6, v6 = wl.make_fwd_inputs(C4D64)
+        gdo6 = torch.Generator().manual_seed(C4D64.seed + 50)
+        do6 = torch.randn(q6.shape, generator=gdo6, dtype=torch.float32).to(q6.dtype)
+        GB6 = [t.to(dev) for t in (q6, k6, v6, do6)]
+        del q6, k6, v6, do6
+        ob6, lb6 = sdpa.attn_fwd(GB6[0], GB6[1], GB6[2], causal=True, stream=stream)
+        dq6, dk6, dv6 = torch.empty_like(GB6[0]), torch.empty_like(GB6[1]), torch.empty_like(GB6[2])
+        ws6 = torch.empty(sdpa.attn_bwd_workspace_bytes(C4D64.B, C4D64.Hq, C4D64.Lq), dtype=torch.uint8, device=dev)
+        calls["bwd_d64"] = lambda: sdpa.attn_bwd(GB6[0], GB6[1], GB6[2], ob6, lb6, GB6[3], causal=True, dq=dq6,
+                                                 dk=dk6, dv=dv6, workspace=ws6, stream=stream)
     fp8_in = {}
     for n, w in (("fwd_fp8_n4096", wl.C7), ("fwd_fp8_causal_n8192", wl.C8)):
         if n in solo:
@@ -416,6 +430,15 @@ def main():
                       "algorithmic_flops": fb,
                       "algorithmic_bytes": wl.algorithmic_bytes_bwd(C4.B, C4.Hq, C4.Hkv, C4.Lq, C4.Lk, C4.d, 2)}
 
+    if "bwd_d64" in ms:
+        t = ms["bwd_d64"] / 1e3
+        w6 = C4D64
+        fb = wl.algorithmic_flops_bwd(w6.B, w6.Hq, w6.Lq, w6.Lk, w6.d, w6.causal)
+        res["bwd_d64"] = {"kernel": "attn_bwd_delta_kernel<64>, then attn_bwd_dq_kernel<64, true> on a second "
+                                    "stream beside attn_bwd_dkdv_kernel<64, true>", "ms": ms["bwd_d64"],
+                          "tflops": fb / t / 1e12, "algorithmic_flops": fb,
+                          "algorithmic_bytes": wl.algorithmic_bytes_bwd(w6.B, w6.Hq, w6.Hkv, w6.Lq, w6.Lk, w6.d, 2)}
+
     if "fwd_masked" in ms:
         t = ms["fwd_masked"] / 1e3
         res["fwd_masked"] = {"kernel": "attn_fwd_bf16_kernel<64, false, 1> (boolean mask, shared by all heads)",
@@ -493,6 +516,9 @@ def main():
     if "bwd" in res:
         r = res["bwd"]
         out["extra"]["bwd_causal_gqa_n8192_d128"] = dict(r, roofline=roof_fwd(r, "attn_bwd_d128_causal_n8192"))
+    if "bwd_d64" in res:
+        r = res["bwd_d64"]
+        out["extra"]["bwd_causal_gqa_n8192_d64"] = dict(r, roofline=roof_fwd(r, "attn_bwd_d64_causal_n8192"))
     if "fwd_fp8_n4096" in res:
         r = res["fwd_fp8_n4096"]
         out["extra"]["fwd_fp8_n4096_d64"] = dict(r, roofline=roof_fwd(r, "attn_fwd_fp8_d64_n4096", PEAK_FP8_TFLOPS))
