@@ -104,3 +104,77 @@ def check_fp8(o, o_ref, lse, lse_ref, sig_o, sig_l, wabs, label: str = ""):
     assert mean_ratio <= 1.0, f"mean O error above the rounding model ({mean_ratio:.3f})"
     assert worst_l <= 1.0, f"LSE outside the e4m3 rounding gate ({worst_l:.3f})"
     return dict(worst=worst, mean_ratio=mean_ratio, worst_lse=worst_l)
+
+
+ROUND_BF16 = 2.0 ** -8  # |bf16(x) - x| <= 2^-8 |x|: half an ulp, round to nearest even
+ROUND_BF16_MEAN = 2.0 ** -9  # mean rounding error of bf16 (ulp / 4), relative
+
+
+def bwd_gate(got, ref, bound=None):
+    """The backward's gate for one gradient tensor against the float64
+    oracle: (worst element's error over its allowance, mean error over the
+    mean allowance, all values finite).  Allowance per element: the stated
+    bf16 tolerance 2e-2, plus the rounding of the result to bf16 (2^-8 |ref|,
+    which gradients cannot avoid since, unlike O, they are not bounded by the
+    values' range), plus `bound` where given (bwd_rounding_bound: the
+    method's own roundings inside the sums).  Mean: 1e-3 + 2^-9 mean |ref|."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = np.abs(got - ref)
+    a = np.abs(ref)
+    allow = BF16_MAX_ABS + ROUND_BF16 * a + (0.0 if bound is None else np.asarray(bound, np.float64))
+    worst = float((d / allow).max()) if d.size else 0.0
+    mean = float(d.mean() / (BF16_MEAN_ABS + ROUND_BF16_MEAN * a.mean())) if d.size else 0.0
+    return worst, mean, bool(np.isfinite(got).all())
+
+
+def bwd_rounding_bound(q, k, v, do, causal: bool, scale=None):
+    """Per-element allowance for what the backward's own roundings move dQ,
+    dK and dV by (part of the gate, not a reference value).
+
+    The backward of "Flash Attention原理：分块计算与重计算" (cnblogs), section
+    五, as the kernel runs it: D = rowsum(dO * O) is formed from the bf16 O
+    that the forward returned (O itself a product of bf16-rounded
+    probabilities), and dS and P are rounded to bf16 before their products.
+    In a gradient that is a sum with much cancellation (a key that every
+    query sees, causal) these move the result by far more than its own
+    output rounding.  Each rounding is taken as an independent error,
+    uniform within +-u |x| (u = 2^-8, half an ulp), so of variance at most
+    s2 x^2 with s2 = u^2 / 3.  From the float64 quantities of the
+    definition, to first order (fp32 accumulation and the exponential's
+    error are orders smaller):
+        var D_q     = s2 (sum_c dO_qc^2 O_qc^2 + sum_j P_qj^2 dP_qj^2)
+                      (O's output rounding; the forward's rounding of P)
+        dS_qj moves by -P_qj dD_q (one dD_q for the whole row) plus its own
+                      rounding, variance s2 dS_qj^2
+        var dQ_qc   = scale^2 (var D_q (sum_j P_qj K_jc)^2 + s2 sum_j dS_qj^2 K_jc^2)
+        var dK_jc   = scale^2 sum_q (P_qj^2 var D_q + s2 dS_qj^2) Q_qc^2
+        var dV_jc   = s2 sum_q P_qj^2 dO_qc^2
+    (dK and dV summed over the kv head's query heads).  The allowance is six
+    standard deviations, as for the FP8 probabilities.  Causal is top-left
+    (query i sees keys j <= i).  Returns arrays shaped like dq, dk, dv."""
+    def f64(t):
+        return np.asarray(to_np(t) if hasattr(t, "detach") else t, np.float64)
+    q, k, v, do = f64(q), f64(k), f64(v), f64(do)
+    B, Hq, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    group = Hq // Hkv
+    sc = d ** -0.5 if scale is None else scale
+    s2 = ROUND_BF16 ** 2 / 3.0
+    vq, vk, vv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    if Lq > 0 and Lk > 0:
+        vis = np.tril(np.ones((Lq, Lk), bool)) if causal else np.ones((Lq, Lk), bool)
+        for b in range(B):
+            for h in range(Hq):
+                kh, vh, qh, doh = k[b, h // group], v[b, h // group], q[b, h], do[b, h]
+                s = np.where(vis, sc * (qh @ kh.T), -np.inf)
+                p = np.where(vis, np.exp(s - s.max(axis=1, keepdims=True)), 0.0)
+                p /= p.sum(axis=1, keepdims=True)
+                o = p @ vh
+                dp = doh @ vh.T
+                ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                var_d = s2 * ((doh ** 2 * o ** 2).sum(axis=1) + (p ** 2 * dp ** 2).sum(axis=1))
+                vq[b, h] = sc ** 2 * (var_d[:, None] * (p @ kh) ** 2 + s2 * (ds ** 2) @ kh ** 2)
+                vk[b, h // group] += sc ** 2 * (p ** 2 * var_d[:, None] + s2 * ds ** 2).T @ qh ** 2
+                vv[b, h // group] += s2 * (p ** 2).T @ doh ** 2
+    return 6.0 * np.sqrt(vq), 6.0 * np.sqrt(vk), 6.0 * np.sqrt(vv)
