@@ -116,15 +116,19 @@ def bwd_gate(got, ref, bound=None):
     mean allowance, all values finite).  Allowance per element: the stated
     bf16 tolerance 2e-2, plus the rounding of the result to bf16 (2^-8 |ref|,
     which gradients cannot avoid since, unlike O, they are not bounded by the
-    values' range), plus `bound` where given (bwd_rounding_bound: the
-    method's own roundings inside the sums).  Mean: 1e-3 + 2^-9 mean |ref|."""
+    values' range), plus `bound` where given (bwd_rounding_bound: six
+    standard deviations of the method's own roundings inside the sums).
+    Mean: 1e-3 + 2^-9 mean |ref|, plus the mean standard deviation (bound / 6)
+    where a bound is given, as the FP8 mean gate takes the mean sigma."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     d = np.abs(got - ref)
     a = np.abs(ref)
-    allow = BF16_MAX_ABS + ROUND_BF16 * a + (0.0 if bound is None else np.asarray(bound, np.float64))
+    bd = 0.0 if bound is None else np.asarray(bound, np.float64)
+    allow = BF16_MAX_ABS + ROUND_BF16 * a + bd
     worst = float((d / allow).max()) if d.size else 0.0
-    mean = float(d.mean() / (BF16_MEAN_ABS + ROUND_BF16_MEAN * a.mean())) if d.size else 0.0
+    mean_allow = BF16_MEAN_ABS + ROUND_BF16_MEAN * a.mean() + (float(np.mean(bd)) / 6.0 if bound is not None else 0.0)
+    mean = float(d.mean() / mean_allow) if d.size else 0.0
     return worst, mean, bool(np.isfinite(got).all())
 
 
