@@ -28,8 +28,10 @@
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
- *     library allocates nothing and keeps no state between calls; the entry
- *     points are thread-safe.
+ *     library allocates no device memory; between calls it keeps only
+ *     memoised device queries, attn_decode_noalloc's static scratch and,
+ *     per device, the stream and two events attn_bwd forks onto (see
+ *     there).  The entry points are thread-safe.
  *   - Sizes and strides are int64 element counts.  The innermost (head_dim)
  *     stride is 1 for every tensor.  Every base pointer must be 16-byte
  *     aligned and every non-innermost stride a multiple of 16 bytes (8 bf16
